@@ -1,0 +1,173 @@
+"""Block allocator model (the bookkeeping half of paged KV caching).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+CPU-baseline leg of the benchmark; never by the product path.
+
+What the pages fix, and where:
+
+* KV memory is cut into equal physical blocks; a sequence's tokens sit in
+  logical blocks [lb*B, lb*B + B) and a per-sequence block table maps logical
+  block -> physical block.  cnblogs "paged attention" sections 2, 3 and 8;
+  "08. PagedAttention", section "borrowing OS paging".
+* Allocation is on demand: prefill takes what it needs, decode takes a new
+  block only when the current one is full (block size 4: 10 tokens use
+  3 blocks, the 11th and 12th still go to logical block 2, the 13th needs a
+  4th block).  cnblogs section 8; "08. PagedAttention", same section.
+* At request end all blocks go back to the free list and are reused at once.
+  cnblogs sections 7 and 8.
+* Sharing by reference counts; copy-on-write when a sequence modifies a
+  shared block: allocate a new block, copy the contents, update the table,
+  decrement the old block's count.  intelliparadigm.com article, section 2.3;
+  "08. PagedAttention", section "what else paging solves".
+* A slot is block_table[logical_block] * block_size + offset.
+  "08. PagedAttention", section "why the name".
+
+Readings where the pages are silent (one fixed policy, so two
+implementations can be compared bit for bit; any free block is as good as
+another):
+
+* The free list is a LIFO stack.  Initially ``init_order[0]`` is on top.
+* ``free`` releases blocks in reverse logical order, so logical block 0 ends
+  on top and re-allocating the same length reproduces the same table.
+* Copy-on-write happens only when the block is shared (ref count > 1) at the
+  sequence's first write into it; the last holder writes in place.
+* ``fork(parent, child, f)`` gives the child the first ceil(f / B) blocks of
+  the parent (ref + 1 each) and length f.
+* ``append`` is atomic: it first counts the blocks it needs and fails with
+  no change when the free list is too short.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+class OutOfBlocks(Exception):
+    pass
+
+
+class AllocatorError(Exception):
+    pass
+
+
+class BlockAllocator:
+    def __init__(self, num_blocks: int, block_size: int, init_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise AllocatorError("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if init_order is None else [int(b) for b in init_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocatorError("init_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        # top of the stack is the end of the list
+        self.free: List[int] = list(reversed(order))
+        self.ref: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+
+    # -- sequence lifecycle -------------------------------------------------
+    def add(self, seq: int) -> None:
+        if seq in self.tables:
+            raise AllocatorError(f"sequence {seq} exists")
+        self.tables[seq] = []
+        self.lens[seq] = 0
+
+    def _pop(self) -> int:
+        return self.free.pop()
+
+    def append(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Reserve slots for ``n`` new tokens of ``seq``.  Returns the slot of
+        each token and the (src, dst) block copies that must happen before
+        the tokens are written."""
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        if n < 0:
+            raise AllocatorError("negative token count")
+        B = self.block_size
+        table = self.tables[seq]
+        start = self.lens[seq]
+        # count first (atomic append)
+        need = 0
+        have = len(table)
+        seen_shared = set()
+        for p in range(start, start + n):
+            lb = p // B
+            if lb >= len(table):
+                if lb >= have:
+                    need += 1
+                    have += 1
+            elif self.ref[table[lb]] > 1 and lb not in seen_shared:
+                seen_shared.add(lb)
+                need += 1
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        slots: List[int] = []
+        copies: List[Tuple[int, int]] = []
+        for p in range(start, start + n):
+            lb = p // B
+            if lb == len(table):
+                b = self._pop()
+                self.ref[b] = 1
+                table.append(b)
+            elif self.ref[table[lb]] > 1:
+                old = table[lb]
+                b = self._pop()
+                copies.append((old, b))
+                self.ref[old] -= 1
+                self.ref[b] = 1
+                table[lb] = b
+            slots.append(table[lb] * B + p % B)
+        self.lens[seq] = start + n
+        return slots, copies
+
+    def fork(self, parent: int, child: int, fork_pos: int) -> None:
+        if parent not in self.tables:
+            raise AllocatorError(f"unknown sequence {parent}")
+        if child in self.tables:
+            raise AllocatorError(f"sequence {child} exists")
+        if not 0 <= fork_pos <= self.lens[parent]:
+            raise AllocatorError("fork position outside the parent")
+        nb = -(-fork_pos // self.block_size)
+        shared = self.tables[parent][:nb]
+        for b in shared:
+            self.ref[b] += 1
+        self.tables[child] = list(shared)
+        self.lens[child] = fork_pos
+
+    def release(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        for b in reversed(self.tables[seq]):
+            if self.ref[b] <= 0:
+                raise AllocatorError("reference count underflow")
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    # -- queries ------------------------------------------------------------
+    def table(self, seq: int) -> List[int]:
+        return list(self.tables[seq])
+
+    def length(self, seq: int) -> int:
+        return self.lens[seq]
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def used_blocks(self) -> set:
+        return {b for b in range(self.num_blocks) if self.ref[b] > 0}
+
+    def block_tables(self, seqs: Sequence[int], width: int):
+        """Padded [len(seqs), width] table (pad -1) and context lengths."""
+        import numpy as np
+
+        t = np.full((len(seqs), max(width, 1)), -1, dtype=np.int32)
+        lens = np.zeros(len(seqs), dtype=np.int32)
+        for i, s in enumerate(seqs):
+            row = self.tables[s]
+            if len(row) > width:
+                raise AllocatorError("table wider than the padded width")
+            t[i, : len(row)] = row
+            lens[i] = self.lens[s]
+        return t, lens
