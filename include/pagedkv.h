@@ -1,0 +1,222 @@
+/*
+ * pagedkv -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * Attention for the current query tokens over a K/V cache that lives in
+ * fixed-size physical blocks and is reached through a per-sequence block
+ * table (cnblogs "paged attention", sections 2, 3 and 5; "08. PagedAttention",
+ * sections "borrowing OS paging" and "why the name").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code; no call throws.
+ *    pkv_status_string() names a code.
+ *  - Device pointers are caller-owned device memory (this library allocates
+ *    no device memory; the caller sizes workspaces with the *_size calls).
+ *    Host pointers are caller-owned host memory and are not retained.
+ *  - GPU calls only enqueue work on `stream` (a hipStream_t; NULL = the
+ *    default stream) and return at once.  Argument checks are synchronous and
+ *    host-side; a failed check enqueues nothing.  A launch failure reports
+ *    PKV_ERR_HIP.
+ *  - Cache layout: k_cache and v_cache are [num_blocks][num_kv_heads]
+ *    [block_size][head_dim] arrays of `dtype` elements.  Token slot s lives in
+ *    physical block s / block_size at offset s % block_size.
+ *  - Block tables are int32 [num_seqs][max_blocks_per_seq]; entry lb is the
+ *    physical block of logical block lb (tokens lb*B .. lb*B+B-1).  Entries
+ *    past ceil(context_len / block_size) are never read (pad them with -1).
+ *    Table contents are trusted: an entry outside [0, num_blocks) is not
+ *    dereferenced; rows that meet one produce NaN outputs.
+ *  - Query head h reads KV head h / (num_heads / num_kv_heads).
+ *  - Device pointers to element arrays must be 16-byte aligned
+ *    (PKV_ERR_ALIGN otherwise); int32 arrays need 4-byte alignment.
+ *  - Supported shapes (PKV_ERR_UNSUPPORTED otherwise): dtype f32 or bf16;
+ *    head_dim 16, 32, 64 or 128; block_size 1, 2, 4, 8, 16, 32 or 64;
+ *    num_heads / num_kv_heads in {1, 2, 4, 8} with head_dim * elem_bytes
+ *    / 16 >= that ratio.  Prefill: bf16, head_dim 64 or 128, block_size 8..64.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+#define PKV_OK 0
+#define PKV_ERR_INVALID (-1)     /* bad argument (null, negative size, bad id) */
+#define PKV_ERR_UNSUPPORTED (-2) /* shape or dtype outside the compiled set */
+#define PKV_ERR_ALIGN (-3)       /* device pointer not 16-byte aligned */
+#define PKV_ERR_NO_BLOCKS (-4)   /* free list too short; state unchanged */
+#define PKV_ERR_STATE (-5)       /* allocator state inconsistent with the request */
+#define PKV_ERR_HIP (-6)         /* a HIP runtime call or kernel launch failed */
+#define PKV_ERR_WORKSPACE (-7)   /* workspace missing or smaller than required */
+
+#define PKV_DTYPE_F32 0
+#define PKV_DTYPE_BF16 1
+
+/* Version of this interface (PKV_ABI_VERSION). */
+int pkv_abi_version(void);
+
+/* Static string naming a status code. */
+const char* pkv_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * kv_write: store each new token's K and V at its slot.
+ * "08. PagedAttention", section "why the name": slot =
+ * block_table[logical block] * block_size + offset, and a small GPU kernel
+ * writes every token's K/V to its slot.
+ *
+ *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim] of dtype
+ *   slot_mapping   device int32 [num_tokens]; a negative slot skips the token;
+ *                  slots must be < num_blocks * block_size and distinct
+ *                  (duplicates race; out-of-range slots are skipped)
+ *   k_cache, v_cache  device caches (layout above), updated in place
+ * Bitwise copy of the token rows; nothing else in the caches changes.
+ * ---------------------------------------------------------------------- */
+int pkv_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                 void* k_cache, void* v_cache, int num_blocks, int num_kv_heads, int block_size,
+                 int head_dim, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * copy_blocks: copy-on-write block copies.  intelliparadigm.com article,
+ * section 2.3: when a sequence modifies a shared block, a new block is
+ * allocated and the original block's contents are copied into it.
+ *
+ *   pairs   device int32 [num_pairs][2] = (src, dst) physical blocks
+ * For each pair, every slot of every head of block dst in both caches becomes
+ * a bitwise copy of block src.  Destinations must be distinct and must not
+ * appear as sources (the allocator below only produces such lists); pairs
+ * with an id outside [0, num_blocks) are skipped.
+ * ---------------------------------------------------------------------- */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int num_blocks,
+                    int num_kv_heads, int block_size, int head_dim, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_decode: one query token per sequence.
+ * out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over the first
+ * context_lens[s] tokens of sequence s, K_s / V_s read through the block
+ * table (cnblogs section 5: position -> logical block -> physical block; the
+ * attention formula itself is unchanged, cnblogs section 6).
+ *
+ *   out            device [num_seqs][num_heads][head_dim] of dtype (written)
+ *   q              device [num_seqs][num_heads][head_dim] of dtype
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   device int32 [num_seqs]; the count includes the token this
+ *                  step wrote.  <= 0 gives zeros; values above
+ *                  max_blocks_per_seq * block_size are clamped to it.
+ *   workspace      device scratch of at least pkv_decode_workspace_size(...)
+ *                  bytes, private to this call until it completes on `stream`
+ * Accumulation is fp32.  Long contexts are split across wavefronts; partial
+ * results are merged with their log-sum-exp weights in a second kernel.
+ * ---------------------------------------------------------------------- */
+size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int dtype);
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_prefill: a causal query chunk over a cached prefix.
+ * Query i of sequence s (rows cu_q_lens[s] .. cu_q_lens[s+1]-1 of q) sits at
+ * position context_lens[s] - C_s + i, C_s = cu_q_lens[s+1] - cu_q_lens[s],
+ * and attends keys 0 .. that position inclusive.  The chunk's K/V must
+ * already be in the cache (pkv_kv_write).  Block-wise computation of scores
+ * and merging of partial results: intelliparadigm.com article, section 2.2.
+ *
+ *   out, q         device [total_q][num_heads][head_dim], bf16
+ *   cu_q_lens      device int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing
+ *   max_q_len      host bound on every C_s (sizes the launch)
+ *   context_lens   device int32 [num_seqs], each >= C_s
+ * ---------------------------------------------------------------------- */
+int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q,
+                                int max_q_len, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                float scale, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator: builds block tables, slot mappings and copy lists.
+ * Never touches the GPU.  Not thread-safe; one handle per owner.
+ *
+ * Policy (the pages fix the semantics; the order is this library's reading
+ * so results are reproducible):
+ *  - free list = LIFO stack; init_order[0] (or block 0) is popped first;
+ *  - append: a new block only when the last one is full (cnblogs section 8);
+ *    the first write into a block shared by several sequences copies it to a
+ *    fresh block (copy-on-write, intelliparadigm.com section 2.3), the last
+ *    holder writes in place;
+ *  - fork(parent, child, f): child shares the parent's first ceil(f/B)
+ *    blocks (ref + 1) and has length f ("08. PagedAttention", section "what
+ *    else paging solves": shared blocks carry a reference count);
+ *  - free: blocks are released in reverse logical order; a block whose
+ *    count reaches 0 goes back on the free list at once (cnblogs section 7).
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_alloc pkv_alloc;
+
+typedef struct pkv_stats {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_free;
+    int32_t num_used;       /* blocks with ref > 0 */
+    int32_t num_seqs;
+    int32_t num_shared;     /* blocks with ref > 1 */
+    int64_t logical_tokens; /* sum of sequence lengths */
+    int64_t table_slots;    /* sum over sequences of table length * block_size */
+} pkv_stats;
+
+/* init_order: host int32 [num_blocks] permutation or NULL (0, 1, 2, ...).
+ * Returns NULL on invalid arguments or out of host memory. */
+pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* init_order);
+void pkv_alloc_destroy(pkv_alloc* a);
+
+/* New empty sequence.  PKV_ERR_INVALID if the id exists. */
+int pkv_seq_add(pkv_alloc* a, int64_t seq);
+
+/* Reserve slots for n new tokens.  slots_out: host int32 [n] (written).
+ * copy_pairs_out: host int32 [copy_cap][2] receiving (src, dst) copies that
+ * must be applied (pkv_copy_blocks) before the tokens are written; one append
+ * produces at most one copy.  *num_copies_out gets the count.  Atomic: on
+ * PKV_ERR_NO_BLOCKS or any error nothing changes. */
+int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t* copy_pairs_out,
+                   int copy_cap, int* num_copies_out);
+
+/* child := first fork_pos tokens of parent, sharing its blocks.
+ * PKV_ERR_INVALID for an unknown parent, an existing child or
+ * fork_pos outside [0, len(parent)]. */
+int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos);
+
+/* Release a sequence.  PKV_ERR_INVALID if unknown; PKV_ERR_STATE on a
+ * reference-count underflow (never happens through this API). */
+int pkv_seq_free(pkv_alloc* a, int64_t seq);
+
+int pkv_seq_len(const pkv_alloc* a, int64_t seq, int64_t* len_out);
+
+/* Copy a sequence's table (host int32 [cap]); *len_out = its length in
+ * blocks.  PKV_ERR_INVALID if cap is too small. */
+int pkv_get_block_table(const pkv_alloc* a, int64_t seq, int32_t* out, int cap, int* len_out);
+
+/* Padded batch export: tables_out host int32 [num_seqs][max_blocks_per_seq]
+ * (pad -1), context_lens_out host int32 [num_seqs]. */
+int pkv_build_block_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs,
+                           int max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
+
+int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out);
+
+/* Inspection for tests: reference count of a block; the free stack from top
+ * to bottom (host int32 [cap]). */
+int pkv_block_ref(const pkv_alloc* a, int block, int* ref_out);
+int pkv_free_list(const pkv_alloc* a, int32_t* out, int cap, int* len_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,175 @@
+// The C ABI: argument checks on the host, then a launch on the caller's
+// stream.  Declarations and their contracts are in include/pagedkv.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "../../include/pagedkv.h"
+#include "kernels.h"
+
+namespace pkv {
+
+const DeviceInfo& device_info() {
+  static DeviceInfo infos[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    static DeviceInfo none;
+    return none;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  DeviceInfo& d = infos[dev];
+  if (!d.ok) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+      d.device = dev;
+      d.num_cus = cus;
+      d.ok = true;
+    }
+  }
+  return d;
+}
+
+int tuning_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (end && *end == 0) ? (int)x : dflt;
+}
+
+}  // namespace pkv
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PKV_DTYPE_F32 ? 4 : dtype == PKV_DTYPE_BF16 ? 2 : 0; }
+
+bool head_dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+bool block_ok(int B) { return pow2(B) && B <= 64; }
+
+// Common checks of the cache geometry.
+int check_cache(int num_blocks, int Hkv, int B, int D, int dtype) {
+  if (num_blocks <= 0 || Hkv <= 0 || B <= 0 || D <= 0) return PKV_ERR_INVALID;
+  if (!elem_bytes(dtype) || !head_dim_ok(D) || !block_ok(B)) return PKV_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * B > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_STATE: return "allocator state error";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int pkv_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens, void* k_cache,
+                 void* v_cache, int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype,
+                 void* stream) {
+  int st = check_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st) return st;
+  if (num_tokens < 0) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(slot_mapping))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_kv_write(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, num_blocks, num_kv_heads,
+                              block_size, head_dim, elem_bytes(dtype), (hipStream_t)stream);
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int num_blocks,
+                    int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  int st = check_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st) return st;
+  if (num_pairs < 0) return PKV_ERR_INVALID;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(pairs)) return PKV_ERR_ALIGN;
+  return pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, num_blocks, num_kv_heads, block_size, head_dim,
+                                 elem_bytes(dtype), (hipStream_t)stream);
+}
+
+static int check_attention(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, int max_blocks, int dtype) {
+  int st = check_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st) return st;
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks <= 0) return PKV_ERR_INVALID;
+  if (num_heads % num_kv_heads) return PKV_ERR_INVALID;
+  if ((long long)max_blocks * block_size > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int dtype) {
+  if (num_kv_heads <= 0) return 0;
+  if (check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, 1, max_blocks_per_seq, dtype))
+    return 0;
+  const int G = num_heads / num_kv_heads;
+  if (!pkv::decode_supported(dtype, head_dim, G)) return 0;
+  if (num_seqs == 0) return 256;
+  return pkv::decode_workspace_bytes(dtype, head_dim, G, num_seqs, num_kv_heads, max_blocks_per_seq, block_size);
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (num_kv_heads <= 0) return PKV_ERR_INVALID;
+  int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           dtype);
+  if (st) return st;
+  const int G = num_heads / num_kv_heads;
+  if (!pkv::decode_supported(dtype, head_dim, G)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || (workspace && !aligned16(workspace)))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_decode(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                            num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
+                            workspace_bytes, (hipStream_t)stream);
+}
+
+int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                                int dtype, void* stream) {
+  if (num_kv_heads <= 0) return PKV_ERR_INVALID;
+  int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           dtype);
+  if (st) return st;
+  if (total_q < 0 || max_q_len < 0) return PKV_ERR_INVALID;
+  const int G = num_heads / num_kv_heads;
+  if (!pkv::prefill_supported(dtype, head_dim, G, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || !aligned4(cu_q_lens))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_prefill(out, q, cu_q_lens, total_q, max_q_len, k_cache, v_cache, block_tables,
+                             max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, scale, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Slot writes and copy-on-write block copies for the paged K/V pools.
+//
+// kv_write: every new token's K and V row goes to its slot, slot =
+// block_table[logical block] * block_size + offset ("08. PagedAttention",
+// section "why the name").  copy_blocks: a destination block becomes a copy
+// of a shared source block before a sequence modifies it (intelliparadigm.com
+// article, section 2.3).  Both are pure data movement; they are bound by HBM
+// bandwidth and move 16 bytes per lane per access, consecutive lanes on
+// consecutive bytes.
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+// One lane per 16-byte piece of a (token, kv head) row, pieces of a row on
+// consecutive lanes: reads of k_new/v_new and writes into the block are both
+// contiguous per row.
+__global__ __launch_bounds__(256) void kv_write_kernel(const char* __restrict__ kn, const char* __restrict__ vn,
+                                                       const int32_t* __restrict__ slots, int num_tokens,
+                                                       char* __restrict__ kc, char* __restrict__ vc, int Hkv,
+                                                       int log2B, int pieces_per_row, long long total_slots) {
+  const int per_tok = Hkv * pieces_per_row;
+  const long long total = (long long)num_tokens * per_tok;
+  const size_t rowb = (size_t)pieces_per_row * 16;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(i / per_tok);
+    const int rem = (int)(i - (long long)t * per_tok);
+    const int h = rem / pieces_per_row;
+    const int pc = rem - h * pieces_per_row;
+    const int slot = slots[t];
+    if (slot < 0 || slot >= total_slots) continue;
+    const int blk = slot >> log2B;
+    const int off = slot & ((1 << log2B) - 1);
+    const size_t dst = ((((size_t)blk * Hkv + h) << log2B) + off) * rowb + (size_t)pc * 16;
+    const size_t src = ((size_t)t * Hkv + h) * rowb + (size_t)pc * 16;
+    const uint4 kx = *(const uint4*)(kn + src);
+    const uint4 vx = *(const uint4*)(vn + src);
+    *(uint4*)(kc + dst) = kx;
+    *(uint4*)(vc + dst) = vx;
+  }
+}
+
+int launch_kv_write(const void* k_new, const void* v_new, const int32_t* slots, int num_tokens, void* k_cache,
+                    void* v_cache, int num_blocks, int Hkv, int B, int D, int elem_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return 0;
+  int log2B = 0;
+  while ((1 << log2B) < B) ++log2B;
+  const int ppr = D * elem_bytes / 16;
+  const long long total = (long long)num_tokens * Hkv * ppr;
+  const DeviceInfo& dev = device_info();
+  long long grid = (total + 255) / 256;
+  const long long cap = (long long)std::max(dev.num_cus, 1) * 16;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const char*)k_new,
+                     (const char*)v_new, slots, num_tokens, (char*)k_cache, (char*)v_cache, Hkv, log2B, ppr,
+                     (long long)num_blocks * B);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// grid.y walks the pairs; grid.x lanes stride over the block's bytes.  A
+// block of one tensor is contiguous: [Hkv][B][D] elements.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs, int num_pairs,
+                                                          int num_blocks, size_t block_bytes) {
+  for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
+    const int src = pairs[2 * p];
+    const int dst = pairs[2 * p + 1];
+    if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) continue;
+    const char* ks = kc + (size_t)src * block_bytes;
+    const char* vs = vc + (size_t)src * block_bytes;
+    char* kd = kc + (size_t)dst * block_bytes;
+    char* vd = vc + (size_t)dst * block_bytes;
+    for (size_t off = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes;
+         off += (size_t)gridDim.x * blockDim.x * 16) {
+      const uint4 a = *(const uint4*)(ks + off);
+      const uint4 b = *(const uint4*)(vs + off);
+      *(uint4*)(kd + off) = a;
+      *(uint4*)(vd + off) = b;
+    }
+  }
+}
+
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int num_blocks, int Hkv,
+                       int B, int D, int elem_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return 0;
+  const size_t block_bytes = (size_t)Hkv * B * D * elem_bytes;
+  unsigned gx = (unsigned)std::min<size_t>((block_bytes / 16 + 255) / 256, 64);
+  if (gx == 0) gx = 1;
+  const unsigned gy = (unsigned)std::min(num_pairs, 65535);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream, (char*)k_cache, (char*)v_cache, pairs,
+                     num_pairs, num_blocks, block_bytes);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // namespace pkv

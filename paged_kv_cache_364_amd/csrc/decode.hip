@@ -1,0 +1,639 @@
+// Paged decode attention for gfx950.
+//
+// Computes out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s where the keys and
+// values of sequence s are found through its block table: position ->
+// logical block -> physical block (cnblogs "paged attention", section 5; the
+// formula itself is unchanged, section 6).  Decode reads the sequence's whole
+// history every step ("08. PagedAttention", section "what it does not
+// solve"), so this kernel is bound by HBM bandwidth.
+//
+// Work split.  The unit of work is a chunk of NT tokens of one (kv head,
+// sequence): NT = 64 / G when a row of K fits in at most 16 lanes, fewer
+// for wider rows so that a chunk never holds more than four 16-byte loads
+// of K and of V per lane.  All chunks of the batch are laid end to end, kv head
+// major, and every wavefront of a persistent grid takes an equal contiguous
+// share (stream-K style), so ragged context lengths do not unbalance the
+// chip.  A (kv head, sequence) whose chunks fall to one wavefront is finished
+// there; one that spans several wavefronts leaves fp32 partials (unnormalised
+// output, running max, running sum) that decode_merge combines with their
+// log-sum-exp weights.  This is the block-wise evaluation with a merge of
+// partial results of the intelliparadigm.com article, section 2.2.
+//
+// Inside a chunk.  Lanes load the K and V rows with coalesced 16-byte loads
+// straight into registers: lane l holds 16 bytes (piece l % LR) of row
+// (l / LR) + j * RW for j < J.  All G query heads of the KV head share those
+// registers (grouped-query attention, cnblogs section 6).  QK^T partial sums
+// are finished by a DPP transpose-reduce inside each row group, leaving each
+// (token, head) score in one lane (or a few identical lanes).  Online softmax state is kept per row group
+// and head; softmax weights reach the P.V lanes through 256 bytes of LDS.
+// P.V accumulates in fp32 registers; row groups are combined once per
+// segment.
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* part;
+  int2* jobs;
+  int S, Hq, Hkv, max_blocks, num_blocks, log2B, nW;
+  float scale_log2;
+};
+
+template <typename T, int D, int G>
+struct DShape {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int E = 16 / ES;       // elements per 16-byte piece
+  static constexpr int LR = D * ES / 16;  // lanes per row
+  static constexpr int RW = 64 / LR;      // rows per wavefront load
+  static constexpr int JMAX = 4;          // loads per chunk and tensor, at most
+  static constexpr int J = (LR / G < JMAX) ? LR / G : JMAX;
+  static constexpr int NT = RW * J;       // tokens per chunk
+  static constexpr int NS = J * G;        // scores per row group and chunk
+  static constexpr int SH = ilog2(LR / NS);  // lanes sharing one score: 1 << SH
+  static constexpr bool FULL_ROWS = LR >= 16;
+  static constexpr int PSZ = G * (D + 2);
+  static constexpr int OPL = (G * D >= 64) ? G * D / 64 : 1;
+  static constexpr int OUT_LANES = G * D / OPL;
+  // LDS (floats): p[RW*NS] | alpha[RW*G] | m[RW*G] | l[RW*G] | acc[RW*G*D]
+  static constexpr int OFF_ALPHA = RW * NS;
+  static constexpr int OFF_M = OFF_ALPHA + RW * G;
+  static constexpr int OFF_L = OFF_M + RW * G;
+  static constexpr int OFF_ACC = OFF_L + RW * G;
+  static constexpr int LDS_FLOATS = OFF_ACC + RW * G * D;
+  static_assert(LR >= G && LR <= 32 && J >= 1 && NS <= LR, "unsupported (dtype, head_dim, group) combination");
+};
+
+constexpr int kWavesPerWG = 4;
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, size_t idx, const float* v, int n);
+
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, size_t idx, const float* v, int n) {
+  float* o = (float*)out + idx;
+  if (n % 4 == 0) {
+    for (int i = 0; i < n; i += 4) *(float4*)(o + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  } else {
+    for (int i = 0; i < n; ++i) o[i] = v[i];
+  }
+}
+
+template <>
+__device__ __forceinline__ void store_out<bf16_t>(void* out, size_t idx, const float* v, int n) {
+  uint16_t* o = (uint16_t*)out + idx;
+  if (n % 8 == 0) {
+    for (int i = 0; i < n; i += 8)
+      *(uint4*)(o + i) = make_uint4(pack_bf16x2(v[i], v[i + 1]), pack_bf16x2(v[i + 2], v[i + 3]),
+                                    pack_bf16x2(v[i + 4], v[i + 5]), pack_bf16x2(v[i + 6], v[i + 7]));
+  } else {
+    for (int i = 0; i < n; ++i) o[i] = (uint16_t)f32_to_bf16(v[i]);
+  }
+}
+
+// Dot product of a 16-byte piece of q and of k.
+template <typename T>
+__device__ __forceinline__ float dot16(const uint4& q, const uint4& k);
+
+template <>
+__device__ __forceinline__ float dot16<bf16_t>(const uint4& q, const uint4& k) {
+  float d = dot2_bf16(q.x, k.x, 0.f);
+  d = dot2_bf16(q.y, k.y, d);
+  d = dot2_bf16(q.z, k.z, d);
+  return dot2_bf16(q.w, k.w, d);
+}
+
+template <>
+__device__ __forceinline__ float dot16<float>(const uint4& q, const uint4& k) {
+  float d = __uint_as_float(q.x) * __uint_as_float(k.x);
+  d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
+  d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
+  return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& v, float* f);
+
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <typename T, int D, int G>
+struct Chunk {
+  uint4 k[DShape<T, D, G>::J];
+  uint4 v[DShape<T, D, G>::J];
+  int ok;   // bit j: row j holds a valid token with a valid block
+  int bad;  // bit j: row j is a valid token whose block id is out of range
+};
+
+// Per-segment state of one wavefront.
+template <typename T, int D, int G>
+struct Seg {
+  using SH = DShape<T, D, G>;
+  const char* kb;  // k_cache + kv head offset (bytes)
+  const char* vb;
+  const int32_t* trow;
+  int ctx;
+  int nblk;   // logical blocks of this context
+  int win;    // table window: lane i holds trow[wbase + i]
+  int wbase;
+  int rg, cl, lane;
+  unsigned loff;  // rg * row bytes + cl * 16
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void refill_window(Seg<T, D, G>& sg, int base) {
+  sg.wbase = base;
+  const int lb = base + sg.lane;
+  sg.win = lb < sg.nblk ? sg.trow[lb] : -1;
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Seg<T, D, G>& sg, const DecodeArgs& a, int c) {
+  using SH = DShape<T, D, G>;
+  const int t0 = c * SH::NT;
+  const int B = 1 << a.log2B;
+  const int lb0 = t0 >> a.log2B;
+  const int lb1 = (min(t0 + SH::NT, sg.ctx) - 1) >> a.log2B;
+  if (lb1 >= sg.wbase + 64 || lb0 < sg.wbase) refill_window(sg, lb0);
+  const size_t rowb = (size_t)D * SH::ES;
+  const size_t blkb = (size_t)a.Hkv << a.log2B;  // rows per physical block (all heads)
+  ch.ok = 0;
+  ch.bad = 0;
+  if (SH::NT <= B) {
+    // the whole chunk lies in one block: one uniform table entry, one
+    // uniform base address, a 32-bit offset per lane
+    const int blk = __builtin_amdgcn_readlane(sg.win, lb0 - sg.wbase);
+    const bool bok = (unsigned)blk < (unsigned)a.num_blocks;
+    const size_t ub = ((size_t)blk * blkb + (size_t)(t0 & (B - 1))) * rowb;
+    const char* kp = sg.kb + ub;
+    const char* vp = sg.vb + ub;
+    const int full = t0 + SH::NT <= sg.ctx;
+#pragma unroll
+    for (int j = 0; j < SH::J; ++j) {
+      const int r = sg.rg + j * SH::RW;
+      const unsigned off = sg.loff + (unsigned)(j * SH::RW * D * SH::ES);
+      if (bok && (full || t0 + r < sg.ctx)) {
+        ch.k[j] = *(const uint4*)(kp + off);
+        ch.v[j] = *(const uint4*)(vp + off);
+        ch.ok |= 1 << j;
+      } else {
+        ch.k[j] = make_uint4(0, 0, 0, 0);
+        ch.v[j] = make_uint4(0, 0, 0, 0);
+        if (t0 + r < sg.ctx) ch.bad |= 1 << j;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SH::J; ++j) {
+      const int t = t0 + sg.rg + j * SH::RW;
+      const int lb = t >> a.log2B;
+      const int blk = __builtin_amdgcn_ds_bpermute((lb - sg.wbase) << 2, sg.win);
+      ch.k[j] = make_uint4(0, 0, 0, 0);
+      ch.v[j] = make_uint4(0, 0, 0, 0);
+      if (t < sg.ctx) {
+        if ((unsigned)blk < (unsigned)a.num_blocks) {
+          const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + sg.cl * 16;
+          ch.k[j] = *(const uint4*)(sg.kb + off);
+          ch.v[j] = *(const uint4*)(sg.vb + off);
+          ch.ok |= 1 << j;
+        } else {
+          ch.bad |= 1 << j;
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const Seg<T, D, G>& sg, const uint4 (&qv)[G],
+                                              float scale_log2, float& m, float& lsum, float (&acc)[G][16 / sizeof(T)],
+                                              float* L) {
+  using SH = DShape<T, D, G>;
+  constexpr int E = SH::E;
+  constexpr int LR = SH::LR;
+  constexpr int NS = SH::NS;
+  // QK^T partial sums over this lane's 16-byte piece: index j*G + g
+  float part[NS];
+#pragma unroll
+  for (int j = 0; j < SH::J; ++j)
+#pragma unroll
+    for (int g = 0; g < G; ++g) part[j * G + g] = dot16<T>(qv[g], ch.k[j]);
+  const float sc = transpose_reduce<NS, LR>(part, sg.cl);
+  // this lane now holds score k = cl >> SH: row j = k / G, head g = k % G
+  const int k = sg.cl >> SH::SH;
+  const int jj = k / G;
+  const bool valid = (ch.ok >> jj) & 1;
+  const bool bad = (ch.bad >> jj) & 1;
+  const float s = valid ? sc * scale_log2 : -INFINITY;
+  const float cmax = group_max<SH::SH + ilog2(G), ilog2(LR), SH::FULL_ROWS>(s);
+  const float mnew = fmaxf(m, cmax);
+  const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+  const float p = valid ? __builtin_amdgcn_exp2f(s - mnew) : 0.f;
+  lsum = lsum * alpha + p + (bad ? __builtin_nanf("") : 0.f);
+  m = mnew;
+  // any head of any row group whose running max moved?
+  const bool rescale = __ballot(alpha != 1.f) != 0;
+  if ((sg.cl & ((1 << SH::SH) - 1)) == 0) {
+    L[sg.rg * NS + k] = p;
+    if (k < G) L[SH::OFF_ALPHA + sg.rg * G + k] = alpha;
+  }
+  wave_lds_sync();
+  float pp[NS];
+  const float* prow = L + sg.rg * NS;
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NS; i += 4) {
+      const float4 x = *(const float4*)(prow + i);
+      pp[i] = x.x; pp[i + 1] = x.y; pp[i + 2] = x.z; pp[i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) pp[i] = prow[i];
+  }
+  if (rescale) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float al = L[SH::OFF_ALPHA + sg.rg * G + g];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] *= al;
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int j = 0; j < SH::J; ++j) {
+    float vf[E];
+    unpack16<T>(ch.v[j], vf);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pp[j * G + g], vf[e], acc[g][e]);
+  }
+}
+
+// mode 0: final output; 1: partial into slot 0; 2: partial into slot 1.
+template <typename T, int D, int G>
+__device__ void process_segment(const DecodeArgs& a, float* L, int lane, int w, int h, int s, int c_lo, int c_hi,
+                                int ctx, int mode) {
+  using SH = DShape<T, D, G>;
+  constexpr int E = SH::E;
+  Seg<T, D, G> sg;
+  sg.lane = lane;
+  sg.rg = lane / SH::LR;
+  sg.cl = lane % SH::LR;
+  sg.loff = (unsigned)(sg.rg * D * SH::ES + sg.cl * 16);
+  sg.ctx = ctx;
+  sg.nblk = (ctx + (1 << a.log2B) - 1) >> a.log2B;
+  sg.trow = a.tables + (size_t)s * a.max_blocks;
+  const size_t rowb = (size_t)D * SH::ES;
+  sg.kb = (const char*)a.k_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
+  sg.vb = (const char*)a.v_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
+  refill_window(sg, (c_lo * SH::NT) >> a.log2B);
+
+  uint4 qv[G];
+  const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + sg.cl * 16;
+#pragma unroll
+  for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qp + g * rowb);
+
+  float m = -INFINITY, lsum = 0.f;
+  float acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+
+  Chunk<T, D, G> ca, cb;
+  load_chunk(ca, sg, a, c_lo);
+  for (int c = c_lo; c < c_hi; c += 2) {
+    if (c + 1 < c_hi) load_chunk(cb, sg, a, c + 1);
+    compute_chunk(ca, sg, qv, a.scale_log2, m, lsum, acc, L);
+    if (c + 1 >= c_hi) break;
+    if (c + 2 < c_hi) load_chunk(ca, sg, a, c + 2);
+    compute_chunk(cb, sg, qv, a.scale_log2, m, lsum, acc, L);
+  }
+
+  // combine the row groups
+  const float lt = group_sum<SH::SH + ilog2(G), ilog2(SH::LR), SH::FULL_ROWS>(lsum);
+  if (sg.cl < (G << SH::SH) && (sg.cl & ((1 << SH::SH) - 1)) == 0) {
+    L[SH::OFF_M + sg.rg * G + (sg.cl >> SH::SH)] = m;
+    L[SH::OFF_L + sg.rg * G + (sg.cl >> SH::SH)] = lt;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float* dst = L + SH::OFF_ACC + (sg.rg * G + g) * D + sg.cl * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+  }
+  wave_lds_sync();
+  if (lane < SH::OUT_LANES) {
+    constexpr int OPL = SH::OPL;
+    const int o0 = lane * OPL;
+    const int g = o0 / D;
+    const int d0 = o0 % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < SH::RW; ++r) M = fmaxf(M, L[SH::OFF_M + r * G + g]);
+    float res[OPL];
+#pragma unroll
+    for (int i = 0; i < OPL; ++i) res[i] = 0.f;
+    float lt_all = 0.f;
+#pragma unroll
+    for (int r = 0; r < SH::RW; ++r) {
+      const float mr = L[SH::OFF_M + r * G + g];
+      const float wr = (mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr - M);
+      lt_all = fmaf(wr, L[SH::OFF_L + r * G + g], lt_all);
+      const float* src = L + SH::OFF_ACC + (r * G + g) * D + d0;
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) res[i] = fmaf(wr, src[i], res[i]);
+    }
+    if (mode == 0) {
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) res[i] = res[i] / lt_all;
+      store_out<T>(a.out, ((size_t)s * a.Hq + (size_t)h * G) * D + o0, res, OPL);
+    } else {
+      float* pp = a.part + ((size_t)w * 2 + (mode - 1)) * SH::PSZ;
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) pp[o0 + i] = res[i];
+      if (d0 == 0) {
+        pp[G * D + g] = M;
+        pp[G * D + G + g] = lt_all;
+      }
+    }
+  }
+  wave_lds_sync();
+}
+
+__device__ __forceinline__ int chunks_of(int ctx, int maxctx, int nt) {
+  ctx = min(ctx, maxctx);
+  return ctx > 0 ? (ctx + nt - 1) / nt : 0;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
+  using SH = DShape<T, D, G>;
+  __shared__ __attribute__((aligned(16))) float lds[kWavesPerWG][SH::LDS_FLOATS];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int wg = blockIdx.x;
+  const int nwg = gridDim.x;
+  // Consecutive work shares go to workgroups on the same XCD (workgroups are
+  // dealt to the 8 XCDs round robin), so sequences adjacent in the batch,
+  // e.g. branches sharing a prompt, meet in one L2.
+  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int w = wg * kWavesPerWG + wid;
+  float* L = lds[wid];
+  const int NT = SH::NT;
+  const int maxctx = a.max_blocks << a.log2B;
+  const int S = a.S;
+
+  // zero the outputs of empty sequences
+  for (int s = w; s < S; s += a.nW) {
+    if (a.ctx_lens[s] <= 0) {
+      const size_t n = (size_t)a.Hq * D;
+      for (size_t i = lane; i < n; i += 64) {
+        float z = 0.f;
+        store_out<T>(a.out, (size_t)s * n + i, &z, 1);
+      }
+    }
+  }
+
+  // chunks per kv head, and this wavefront's share
+  int W1 = 0;
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    W1 += wave_sum_i(s < S ? chunks_of(a.ctx_lens[s], maxctx, NT) : 0);
+  }
+  const int Wtot = a.Hkv * W1;
+  const int cpw = (Wtot + a.nW - 1) / max(a.nW, 1);
+  const int gstart = w * cpw;
+  const int gend = min(Wtot, gstart + cpw);
+  if (w >= a.nW) return;
+  if (gstart >= gend) {
+    if (lane == 0) a.jobs[w] = make_int2(-1, 0);
+    return;
+  }
+  int h = gstart / W1;
+  const int rem = gstart - h * W1;
+  int s = 0, P = 0;
+  bool found = false;
+  for (int base = 0; base < S; base += 64) {
+    const int si = base + lane;
+    const int n = si < S ? chunks_of(a.ctx_lens[si], maxctx, NT) : 0;
+    const int incl = wave_incl_scan_i(n, lane);
+    const unsigned long long hit = __ballot(P + incl > rem);
+    if (hit) {
+      const int first = __ffsll((long long)hit) - 1;
+      s = base + first;
+      P += __shfl(incl - n, first);
+      found = true;
+      break;
+    }
+    P += __shfl(incl, 63);
+  }
+  if (!found) {  // context lengths changed under the kernel: do nothing
+    if (lane == 0) a.jobs[w] = make_int2(-1, 0);
+    return;
+  }
+  int c = rem - P;
+  int gpos = gstart;
+  int job_unit = -1, job_last = 0;
+  while (gpos < gend && h < a.Hkv) {
+    const int ctx = min(a.ctx_lens[s], maxctx);
+    const int n = ctx > 0 ? (ctx + NT - 1) / NT : 0;
+    if (n > 0) {
+      const int take = min(n - c, gend - gpos);
+      const int c_end = c + take;
+      const int mode = c > 0 ? 1 : (c_end < n ? 2 : 0);
+      process_segment<T, D, G>(a, L, lane, w, h, s, c, c_end, ctx, mode);
+      if (mode == 2) {
+        job_unit = h * S + s;
+        job_last = (gpos - c + n - 1) / cpw;
+      }
+      gpos += take;
+    }
+    c = 0;
+    if (++s == S) {
+      s = 0;
+      ++h;
+    }
+  }
+  if (lane == 0) a.jobs[w] = make_int2(job_unit, job_last);
+}
+
+// Second pass: log-sum-exp merge of the partials of every (kv head,
+// sequence) that spans several wavefronts.  Job w lists the unit whose first
+// partial wavefront w wrote into slot 1 and the last wavefront holding one;
+// the wavefronts in between wrote theirs into slot 0.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  using SH = DShape<T, D, G>;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+  if (w >= a.nW) return;
+  const int2 job = a.jobs[w];
+  if (job.x < 0 || lane >= SH::OUT_LANES) return;
+  const int h = job.x / a.S;
+  const int s = job.x - h * a.S;
+  constexpr int OPL = SH::OPL;
+  const int o0 = lane * OPL;
+  const int g = o0 / D;
+  auto slot = [&](int k) -> const float* {
+    return a.part + ((size_t)(w + k) * 2 + (k == 0 ? 1 : 0)) * SH::PSZ;
+  };
+  const int K = job.y - w + 1;
+  float M = -INFINITY;
+  for (int k = 0; k < K; ++k) M = fmaxf(M, slot(k)[G * D + g]);
+  float res[OPL];
+#pragma unroll
+  for (int i = 0; i < OPL; ++i) res[i] = 0.f;
+  float lt = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const float* p = slot(k);
+    const float mk = p[G * D + g];
+    const float wk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+    lt = fmaf(wk, p[G * D + G + g], lt);
+#pragma unroll
+    for (int i = 0; i < OPL; ++i) res[i] = fmaf(wk, p[o0 + i], res[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < OPL; ++i) res[i] = res[i] / lt;
+  store_out<T>(a.out, ((size_t)s * a.Hq + (size_t)h * G) * D + o0, res, OPL);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct DecodeKernels {
+  const void* main;
+  const void* merge;
+  int nt;
+  int psz;
+};
+
+template <typename T, int D, int G>
+static DecodeKernels kernels_for() {
+  using SH = DShape<T, D, G>;
+  return {(const void*)decode_main<T, D, G>, (const void*)decode_merge<T, D, G>, SH::NT, SH::PSZ};
+}
+
+static bool pick(int dtype, int D, int G, DecodeKernels* k) {
+#define PKV_CASE(TT, DD, GG)                      \
+  if (D == DD && G == GG) {                       \
+    *k = kernels_for<TT, DD, GG>();               \
+    return true;                                  \
+  }
+  if (dtype == 1) {
+    PKV_CASE(bf16_t, 16, 1) PKV_CASE(bf16_t, 16, 2)
+    PKV_CASE(bf16_t, 32, 1) PKV_CASE(bf16_t, 32, 2) PKV_CASE(bf16_t, 32, 4)
+    PKV_CASE(bf16_t, 64, 1) PKV_CASE(bf16_t, 64, 2) PKV_CASE(bf16_t, 64, 4) PKV_CASE(bf16_t, 64, 8)
+    PKV_CASE(bf16_t, 128, 1) PKV_CASE(bf16_t, 128, 2) PKV_CASE(bf16_t, 128, 4) PKV_CASE(bf16_t, 128, 8)
+  } else if (dtype == 0) {
+    PKV_CASE(float, 16, 1) PKV_CASE(float, 16, 2) PKV_CASE(float, 16, 4)
+    PKV_CASE(float, 32, 1) PKV_CASE(float, 32, 2) PKV_CASE(float, 32, 4) PKV_CASE(float, 32, 8)
+    PKV_CASE(float, 64, 1) PKV_CASE(float, 64, 2) PKV_CASE(float, 64, 4) PKV_CASE(float, 64, 8)
+    PKV_CASE(float, 128, 1) PKV_CASE(float, 128, 2) PKV_CASE(float, 128, 4) PKV_CASE(float, 128, 8)
+  }
+#undef PKV_CASE
+  return false;
+}
+
+bool decode_supported(int dtype, int head_dim, int group) {
+  DecodeKernels k;
+  return pick(dtype, head_dim, group, &k);
+}
+
+// Number of wavefronts of the persistent grid: every resident slot of the
+// device (bounded by a tuning cap), never more than the chunks there can be.
+static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B) {
+  const DeviceInfo& dev = device_info();
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 64 * kWavesPerWG, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int cap = tuning_int("PKV_DECODE_WG_PER_CU", 0);
+  if (cap > 0) per_cu = std::min(per_cu, cap);
+  long long wgs = (long long)per_cu * dev.num_cus;
+  const long long maxctx = (long long)max_blocks * B;
+  const long long upper = (long long)Hkv * S * ((maxctx + k.nt - 1) / k.nt);
+  long long need_wg = (upper + kWavesPerWG - 1) / kWavesPerWG;
+  if (need_wg < wgs) wgs = need_wg;
+  if (wgs < 1) wgs = 1;
+  if (wgs > 8) wgs = wgs / 8 * 8;
+  return (int)(wgs * kWavesPerWG);
+}
+
+size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_blocks, int B) {
+  DecodeKernels k;
+  if (!pick(dtype, D, G, &k)) return 0;
+  const int nW = decode_waves(k, S, Hkv, max_blocks, B);
+  const size_t part = (size_t)nW * 2 * k.psz * sizeof(float);
+  return ((part + 255) / 256) * 256 + (size_t)nW * sizeof(int2);
+}
+
+int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
+                  int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
+                  float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DecodeKernels k;
+  if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
+  const int nW = decode_waves(k, S, Hkv, max_blocks, B);
+  const size_t part = (size_t)nW * 2 * k.psz * sizeof(float);
+  const size_t need = ((part + 255) / 256) * 256 + (size_t)nW * sizeof(int2);
+  if (ws == nullptr || ws_bytes < need) return -7;
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = tables;
+  a.ctx_lens = ctx;
+  a.part = (float*)ws;
+  a.jobs = (int2*)((char*)ws + ((part + 255) / 256) * 256);
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.log2B = 0;
+  while ((1 << a.log2B) < B) ++a.log2B;
+  a.nW = nW;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int grid = nW / kWavesPerWG;
+  hipLaunchKernelGGL((void (*)(DecodeArgs))k.main, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return -6;
+  hipLaunchKernelGGL((void (*)(DecodeArgs))k.merge, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return -6;
+  return 0;
+}
+
+}  // namespace pkv
