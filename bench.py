@@ -38,6 +38,9 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before timing, copy this many MiB once with copy_blocks (a plain copy of known size, "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -88,6 +91,18 @@ def main():
         api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
         if ev is not None:
             ev[2].record()
+
+    if args.calibrate_copy_mib > 0:
+        # n source blocks -> n destination blocks of 64 KiB (K + V): n * 64 KiB read and written
+        n = max(1, args.calibrate_copy_mib * 1024 * 1024 // (2 * Hkv * B * D * 2))
+        ck = torch.zeros((2 * n, Hkv, B, D), dtype=q.dtype, device=dev)
+        cv = torch.zeros_like(ck)
+        pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], 1).to(torch.int32).to(dev).contiguous()
+        torch.cuda.synchronize()
+        api.copy_blocks(ck, cv, pairs)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} block pairs, {2 * n * Hkv * B * D * 2} bytes read and written")
+        del ck, cv
 
     for i in range(args.warmup):
         step(i)

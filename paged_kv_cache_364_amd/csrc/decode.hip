@@ -15,9 +15,15 @@
 // share (stream-K style), so ragged context lengths do not unbalance the
 // chip.  A (kv head, sequence) whose chunks fall to one wavefront is finished
 // there; one that spans several wavefronts leaves fp32 partials (unnormalised
-// output, running max, running sum) that decode_merge combines with their
-// log-sum-exp weights.  This is the block-wise evaluation with a merge of
-// partial results of the intelliparadigm.com article, section 2.2.
+// output, running max, running sum) in the workspace, and a second kernel
+// combines them with their log-sum-exp weights.  This is the block-wise
+// evaluation with a merge of partial results of the intelliparadigm.com
+// article, section 2.2.
+//
+// Each wavefront walks its share as one pipelined stream of chunks: the
+// loads of chunk i + 1 are in flight while chunk i is computed, also across
+// the boundary between two (kv head, sequence) units, whose block-table
+// window and query rows are fetched as soon as the previous unit starts.
 //
 // Inside a chunk.  Lanes load the K and V rows with coalesced 16-byte loads
 // straight into registers: lane l holds 16 bytes (piece l % LR) of row
@@ -40,8 +46,8 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* part;
-  int2* jobs;
+  float* part;  // two partial slots of PSZ floats per wavefront
+  int2* jobs;   // per wavefront: (unit, last wavefront) of the unit it starts, or (-1, 0)
   int S, Hq, Hkv, max_blocks, num_blocks, log2B, nW;
   float scale_log2;
 };
@@ -157,36 +163,73 @@ struct Chunk {
   int bad;  // bit j: row j is a valid token whose block id is out of range
 };
 
-// Per-segment state of one wavefront.
+// One (kv head, sequence) unit as a wavefront sees it.  Lane i of win0 /
+// win1 holds table entry wbase + i / wbase + 64 + i (-1 past the context).
 template <typename T, int D, int G>
-struct Seg {
-  using SH = DShape<T, D, G>;
+struct Unit {
   const char* kb;  // k_cache + kv head offset (bytes)
   const char* vb;
   const int32_t* trow;
-  int ctx;
-  int nblk;   // logical blocks of this context
-  int win;    // table window: lane i holds trow[wbase + i]
-  int wbase;
-  int rg, cl, lane;
-  unsigned loff;  // rg * row bytes + cl * 16
+  int h, s, ctx, n, g0;  // n chunks, the first of which is global chunk g0
+  int nblk, wbase;
+  int win0, win1;
+  uint4 qv[G];
 };
 
 template <typename T, int D, int G>
-__device__ __forceinline__ void refill_window(Seg<T, D, G>& sg, int base) {
-  sg.wbase = base;
-  const int lb = base + sg.lane;
-  sg.win = lb < sg.nblk ? sg.trow[lb] : -1;
+__device__ __forceinline__ int load_window(const Unit<T, D, G>& u, int base, int lane) {
+  const int lb = base + lane;
+  return lb < u.nblk ? u.trow[lb] : -1;
 }
 
+// Set up unit (h, s) starting at global chunk g0: issue the loads of its
+// table window and query rows (nothing waits for them here).
 template <typename T, int D, int G>
-__device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Seg<T, D, G>& sg, const DecodeArgs& a, int c) {
+__device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a, int h, int s, int ctx, int g0,
+                                          int c0, int lane) {
   using SH = DShape<T, D, G>;
+  const size_t rowb = (size_t)D * SH::ES;
+  u.h = h;
+  u.s = s;
+  u.ctx = ctx;
+  u.n = (ctx + SH::NT - 1) / SH::NT;
+  u.g0 = g0;
+  u.nblk = (ctx + (1 << a.log2B) - 1) >> a.log2B;
+  u.trow = a.tables + (size_t)s * a.max_blocks;
+  u.kb = (const char*)a.k_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
+  u.vb = (const char*)a.v_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
+  u.wbase = (c0 * SH::NT) >> a.log2B;
+  u.win0 = load_window(u, u.wbase, lane);
+  u.win1 = load_window(u, u.wbase + 64, lane);
+  const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + (lane % SH::LR) * 16;
+#pragma unroll
+  for (int g = 0; g < G; ++g) u.qv[g] = *(const uint4*)(qp + g * rowb);
+}
+
+// Issue the loads of chunk c of unit u.  Rows past the context, or whose
+// block id is out of range, are zero; the latter are flagged so that the
+// output turns into NaN instead of reading outside the pool.
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u, const DecodeArgs& a, int c,
+                                           int lane) {
+  using SH = DShape<T, D, G>;
+  const int rg = lane / SH::LR;
+  const int cl = lane % SH::LR;
   const int t0 = c * SH::NT;
   const int B = 1 << a.log2B;
   const int lb0 = t0 >> a.log2B;
-  const int lb1 = (min(t0 + SH::NT, sg.ctx) - 1) >> a.log2B;
-  if (lb1 >= sg.wbase + 64 || lb0 < sg.wbase) refill_window(sg, lb0);
+  // slide the window once the chunk has moved into its upper half; the new
+  // upper half is needed only 64 blocks later
+  if (lb0 >= u.wbase + 64) {
+    if (lb0 >= u.wbase + 128) {  // jumped past both halves
+      u.wbase = lb0;
+      u.win0 = load_window(u, u.wbase, lane);
+    } else {
+      u.wbase += 64;
+      u.win0 = u.win1;
+    }
+    u.win1 = load_window(u, u.wbase + 64, lane);
+  }
   const size_t rowb = (size_t)D * SH::ES;
   const size_t blkb = (size_t)a.Hkv << a.log2B;  // rows per physical block (all heads)
   ch.ok = 0;
@@ -194,39 +237,43 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Seg<T, D, G>& sg,
   if (SH::NT <= B) {
     // the whole chunk lies in one block: one uniform table entry, one
     // uniform base address, a 32-bit offset per lane
-    const int blk = __builtin_amdgcn_readlane(sg.win, lb0 - sg.wbase);
+    const int wi = lb0 - u.wbase;
+    const int blk = wi < 64 ? __builtin_amdgcn_readlane(u.win0, wi) : __builtin_amdgcn_readlane(u.win1, wi - 64);
     const bool bok = (unsigned)blk < (unsigned)a.num_blocks;
     const size_t ub = ((size_t)blk * blkb + (size_t)(t0 & (B - 1))) * rowb;
-    const char* kp = sg.kb + ub;
-    const char* vp = sg.vb + ub;
-    const int full = t0 + SH::NT <= sg.ctx;
+    const char* kp = u.kb + ub;
+    const char* vp = u.vb + ub;
+    const int full = t0 + SH::NT <= u.ctx;
+    const unsigned loff = (unsigned)(rg * D * SH::ES + cl * 16);
 #pragma unroll
     for (int j = 0; j < SH::J; ++j) {
-      const int r = sg.rg + j * SH::RW;
-      const unsigned off = sg.loff + (unsigned)(j * SH::RW * D * SH::ES);
-      if (bok && (full || t0 + r < sg.ctx)) {
+      const int r = rg + j * SH::RW;
+      const unsigned off = loff + (unsigned)(j * SH::RW * D * SH::ES);
+      if (bok && (full || t0 + r < u.ctx)) {
         ch.k[j] = *(const uint4*)(kp + off);
         ch.v[j] = *(const uint4*)(vp + off);
         ch.ok |= 1 << j;
       } else {
         ch.k[j] = make_uint4(0, 0, 0, 0);
         ch.v[j] = make_uint4(0, 0, 0, 0);
-        if (t0 + r < sg.ctx) ch.bad |= 1 << j;
+        if (t0 + r < u.ctx) ch.bad |= 1 << j;
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < SH::J; ++j) {
-      const int t = t0 + sg.rg + j * SH::RW;
-      const int lb = t >> a.log2B;
-      const int blk = __builtin_amdgcn_ds_bpermute((lb - sg.wbase) << 2, sg.win);
+      const int t = t0 + rg + j * SH::RW;
+      const int wi = (t >> a.log2B) - u.wbase;  // 0 .. 127 for rows inside the context
+      const int b0 = __builtin_amdgcn_ds_bpermute((wi & 63) << 2, u.win0);
+      const int b1 = __builtin_amdgcn_ds_bpermute((wi & 63) << 2, u.win1);
+      const int blk = wi < 64 ? b0 : b1;
       ch.k[j] = make_uint4(0, 0, 0, 0);
       ch.v[j] = make_uint4(0, 0, 0, 0);
-      if (t < sg.ctx) {
+      if (t < u.ctx) {
         if ((unsigned)blk < (unsigned)a.num_blocks) {
-          const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + sg.cl * 16;
-          ch.k[j] = *(const uint4*)(sg.kb + off);
-          ch.v[j] = *(const uint4*)(sg.vb + off);
+          const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + cl * 16;
+          ch.k[j] = *(const uint4*)(u.kb + off);
+          ch.v[j] = *(const uint4*)(u.vb + off);
           ch.ok |= 1 << j;
         } else {
           ch.bad |= 1 << j;
@@ -236,23 +283,28 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Seg<T, D, G>& sg,
   }
 }
 
+// Online-softmax update with one chunk: scores of the chunk's rows for the
+// G heads, running max m and sum lsum per (row group, head), and the
+// rescaled P.V accumulation.
 template <typename T, int D, int G>
-__device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const Seg<T, D, G>& sg, const uint4 (&qv)[G],
-                                              float scale_log2, float& m, float& lsum, float (&acc)[G][16 / sizeof(T)],
-                                              float* L) {
+__device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const uint4 (&qv)[G], int lane,
+                                              float scale_log2, float& m, float& lsum,
+                                              float (&acc)[G][16 / sizeof(T)], float* L) {
   using SH = DShape<T, D, G>;
   constexpr int E = SH::E;
   constexpr int LR = SH::LR;
   constexpr int NS = SH::NS;
+  const int rg = lane / LR;
+  const int cl = lane % LR;
   // QK^T partial sums over this lane's 16-byte piece: index j*G + g
   float part[NS];
 #pragma unroll
   for (int j = 0; j < SH::J; ++j)
 #pragma unroll
     for (int g = 0; g < G; ++g) part[j * G + g] = dot16<T>(qv[g], ch.k[j]);
-  const float sc = transpose_reduce<NS, LR>(part, sg.cl);
+  const float sc = transpose_reduce<NS, LR>(part, cl);
   // this lane now holds score k = cl >> SH: row j = k / G, head g = k % G
-  const int k = sg.cl >> SH::SH;
+  const int k = cl >> SH::SH;
   const int jj = k / G;
   const bool valid = (ch.ok >> jj) & 1;
   const bool bad = (ch.bad >> jj) & 1;
@@ -265,13 +317,13 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const Se
   m = mnew;
   // any head of any row group whose running max moved?
   const bool rescale = __ballot(alpha != 1.f) != 0;
-  if ((sg.cl & ((1 << SH::SH) - 1)) == 0) {
-    L[sg.rg * NS + k] = p;
-    if (k < G) L[SH::OFF_ALPHA + sg.rg * G + k] = alpha;
+  if ((cl & ((1 << SH::SH) - 1)) == 0) {
+    L[rg * NS + k] = p;
+    if (k < G) L[SH::OFF_ALPHA + rg * G + k] = alpha;
   }
   wave_lds_sync();
   float pp[NS];
-  const float* prow = L + sg.rg * NS;
+  const float* prow = L + rg * NS;
   if constexpr (NS % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < NS; i += 4) {
@@ -285,7 +337,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const Se
   if (rescale) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float al = L[SH::OFF_ALPHA + sg.rg * G + g];
+      const float al = L[SH::OFF_ALPHA + rg * G + g];
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[g][e] *= al;
     }
@@ -302,56 +354,24 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const Se
   }
 }
 
-// mode 0: final output; 1: partial into slot 0; 2: partial into slot 1.
+// End of a segment: combine the row groups' (m, lsum, acc) and write either
+// the normalised output (mode 0) or an unnormalised partial with its max and
+// sum into slot 0 (mode 1) or slot 1 (mode 2) of wavefront w.
 template <typename T, int D, int G>
-__device__ void process_segment(const DecodeArgs& a, float* L, int lane, int w, int h, int s, int c_lo, int c_hi,
-                                int ctx, int mode) {
+__device__ __forceinline__ void finish_segment(const DecodeArgs& a, float* L, int lane, int w, int h, int s,
+                                               int mode, float m, float lsum, const float (&acc)[G][16 / sizeof(T)]) {
   using SH = DShape<T, D, G>;
   constexpr int E = SH::E;
-  Seg<T, D, G> sg;
-  sg.lane = lane;
-  sg.rg = lane / SH::LR;
-  sg.cl = lane % SH::LR;
-  sg.loff = (unsigned)(sg.rg * D * SH::ES + sg.cl * 16);
-  sg.ctx = ctx;
-  sg.nblk = (ctx + (1 << a.log2B) - 1) >> a.log2B;
-  sg.trow = a.tables + (size_t)s * a.max_blocks;
-  const size_t rowb = (size_t)D * SH::ES;
-  sg.kb = (const char*)a.k_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
-  sg.vb = (const char*)a.v_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
-  refill_window(sg, (c_lo * SH::NT) >> a.log2B);
-
-  uint4 qv[G];
-  const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + sg.cl * 16;
-#pragma unroll
-  for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qp + g * rowb);
-
-  float m = -INFINITY, lsum = 0.f;
-  float acc[G][E];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
-
-  Chunk<T, D, G> ca, cb;
-  load_chunk(ca, sg, a, c_lo);
-  for (int c = c_lo; c < c_hi; c += 2) {
-    if (c + 1 < c_hi) load_chunk(cb, sg, a, c + 1);
-    compute_chunk(ca, sg, qv, a.scale_log2, m, lsum, acc, L);
-    if (c + 1 >= c_hi) break;
-    if (c + 2 < c_hi) load_chunk(ca, sg, a, c + 2);
-    compute_chunk(cb, sg, qv, a.scale_log2, m, lsum, acc, L);
-  }
-
-  // combine the row groups
+  const int rg = lane / SH::LR;
+  const int cl = lane % SH::LR;
   const float lt = group_sum<SH::SH + ilog2(G), ilog2(SH::LR), SH::FULL_ROWS>(lsum);
-  if (sg.cl < (G << SH::SH) && (sg.cl & ((1 << SH::SH) - 1)) == 0) {
-    L[SH::OFF_M + sg.rg * G + (sg.cl >> SH::SH)] = m;
-    L[SH::OFF_L + sg.rg * G + (sg.cl >> SH::SH)] = lt;
+  if (cl < (G << SH::SH) && (cl & ((1 << SH::SH) - 1)) == 0) {
+    L[SH::OFF_M + rg * G + (cl >> SH::SH)] = m;
+    L[SH::OFF_L + rg * G + (cl >> SH::SH)] = lt;
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float* dst = L + SH::OFF_ACC + (sg.rg * G + g) * D + sg.cl * E;
+    float* dst = L + SH::OFF_ACC + (rg * G + g) * D + cl * E;
 #pragma unroll
     for (int e = 0; e < E; e += 4) *(float4*)(dst + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
   }
@@ -383,8 +403,13 @@ __device__ void process_segment(const DecodeArgs& a, float* L, int lane, int w, 
       store_out<T>(a.out, ((size_t)s * a.Hq + (size_t)h * G) * D + o0, res, OPL);
     } else {
       float* pp = a.part + ((size_t)w * 2 + (mode - 1)) * SH::PSZ;
+      if constexpr (OPL % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < OPL; ++i) pp[o0 + i] = res[i];
+        for (int i = 0; i < OPL; i += 4) *(float4*)(pp + o0 + i) = make_float4(res[i], res[i + 1], res[i + 2], res[i + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < OPL; ++i) pp[o0 + i] = res[i];
+      }
       if (d0 == 0) {
         pp[G * D + g] = M;
         pp[G * D + G + g] = lt_all;
@@ -399,9 +424,22 @@ __device__ __forceinline__ int chunks_of(int ctx, int maxctx, int nt) {
   return ctx > 0 ? (ctx + nt - 1) / nt : 0;
 }
 
+// Next non-empty unit after (h, s) in kv-head-major order; false at the end.
+__device__ __forceinline__ bool next_unit(const DecodeArgs& a, int maxctx, int& h, int& s, int& ctx) {
+  for (;;) {
+    if (++s == a.S) {
+      s = 0;
+      if (++h == a.Hkv) return false;
+    }
+    ctx = min(a.ctx_lens[s], maxctx);
+    if (ctx > 0) return true;
+  }
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   using SH = DShape<T, D, G>;
+  constexpr int E = SH::E;
   __shared__ __attribute__((aligned(16))) float lds[kWavesPerWG][SH::LDS_FLOATS];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -413,9 +451,11 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
   const int w = wg * kWavesPerWG + wid;
   float* L = lds[wid];
-  const int NT = SH::NT;
+  constexpr int NT = SH::NT;
   const int maxctx = a.max_blocks << a.log2B;
   const int S = a.S;
+  if (w >= a.nW) return;
+  if (lane == 0) a.jobs[w] = make_int2(-1, 0);
 
   // zero the outputs of empty sequences
   for (int s = w; s < S; s += a.nW) {
@@ -428,7 +468,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     }
   }
 
-  // chunks per kv head, and this wavefront's share
+  // chunks per kv head, and this wavefront's share [gstart, gend)
   int W1 = 0;
   for (int base = 0; base < S; base += 64) {
     const int s = base + lane;
@@ -438,11 +478,8 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   const int cpw = (Wtot + a.nW - 1) / max(a.nW, 1);
   const int gstart = w * cpw;
   const int gend = min(Wtot, gstart + cpw);
-  if (w >= a.nW) return;
-  if (gstart >= gend) {
-    if (lane == 0) a.jobs[w] = make_int2(-1, 0);
-    return;
-  }
+  if (gstart >= gend) return;
+  // locate the unit holding chunk gstart
   int h = gstart / W1;
   const int rem = gstart - h * W1;
   int s = 0, P = 0;
@@ -461,40 +498,74 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     }
     P += __shfl(incl, 63);
   }
-  if (!found) {  // context lengths changed under the kernel: do nothing
-    if (lane == 0) a.jobs[w] = make_int2(-1, 0);
-    return;
-  }
-  int c = rem - P;
-  int gpos = gstart;
-  int job_unit = -1, job_last = 0;
-  while (gpos < gend && h < a.Hkv) {
-    const int ctx = min(a.ctx_lens[s], maxctx);
-    const int n = ctx > 0 ? (ctx + NT - 1) / NT : 0;
-    if (n > 0) {
-      const int take = min(n - c, gend - gpos);
-      const int c_end = c + take;
-      const int mode = c > 0 ? 1 : (c_end < n ? 2 : 0);
-      process_segment<T, D, G>(a, L, lane, w, h, s, c, c_end, ctx, mode);
-      if (mode == 2) {
-        job_unit = h * S + s;
-        job_last = (gpos - c + n - 1) / cpw;
-      }
-      gpos += take;
+  if (!found) return;  // context lengths changed under the kernel: do nothing
+
+  Unit<T, D, G> cur, nxt;
+  int c = rem - P;  // chunk of `cur` being computed
+  open_unit(cur, a, h, s, min(a.ctx_lens[s], maxctx), gstart - c, c, lane);
+  int seg_c0 = c;  // first chunk of cur in this wavefront's share
+  bool have_next = false;
+  {
+    int h2 = h, s2 = s, ctx2 = 0;
+    if (cur.g0 + cur.n < gend && next_unit(a, maxctx, h2, s2, ctx2)) {
+      open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
+      have_next = true;
     }
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  float acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+
+  // One step: prefetch the chunk after `i` into `nb`, compute chunk i from
+  // `cb`, and close the unit when its last chunk (or the share) ends.
+  // Returns false when the share is done.
+  auto step = [&](Chunk<T, D, G>& cb, Chunk<T, D, G>& nb, int i) -> bool {
+    if (i + 1 < gend) {
+      if (c + 1 < cur.n) load_chunk(nb, cur, a, c + 1, lane);
+      else load_chunk(nb, nxt, a, 0, lane);
+    }
+    compute_chunk<T, D, G>(cb, cur.qv, lane, a.scale_log2, m, lsum, acc, L);
+    ++c;
+    if (c < cur.n && i + 1 < gend) return true;
+    const int mode = seg_c0 > 0 ? 1 : (c < cur.n ? 2 : 0);
+    finish_segment<T, D, G>(a, L, lane, w, cur.h, cur.s, mode, m, lsum, acc);
+    if (mode == 2 && lane == 0) a.jobs[w] = make_int2(cur.h * S + cur.s, (cur.g0 + cur.n - 1) / cpw);
+    if (i + 1 >= gend || !have_next) return false;
+    cur = nxt;
     c = 0;
-    if (++s == S) {
-      s = 0;
-      ++h;
+    seg_c0 = 0;
+    have_next = false;
+    int h2 = cur.h, s2 = cur.s, ctx2 = 0;
+    if (cur.g0 + cur.n < gend && next_unit(a, maxctx, h2, s2, ctx2)) {
+      open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
+      have_next = true;
     }
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+    return true;
+  };
+
+  Chunk<T, D, G> ca, cb;
+  load_chunk(ca, cur, a, c, lane);
+  for (int i = gstart; i < gend; i += 2) {
+    if (!step(ca, cb, i)) break;
+    if (i + 1 >= gend || !step(cb, ca, i + 1)) break;
   }
-  if (lane == 0) a.jobs[w] = make_int2(job_unit, job_last);
 }
 
 // Second pass: log-sum-exp merge of the partials of every (kv head,
-// sequence) that spans several wavefronts.  Job w lists the unit whose first
+// sequence) that spans several wavefronts.  Job w names the unit whose first
 // partial wavefront w wrote into slot 1 and the last wavefront holding one;
-// the wavefronts in between wrote theirs into slot 0.
+// the wavefronts in between wrote theirs into slot 0.  All loads of a pass
+// are issued before any is used.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   using SH = DShape<T, D, G>;
@@ -508,23 +579,56 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   constexpr int OPL = SH::OPL;
   const int o0 = lane * OPL;
   const int g = o0 / D;
+  const int K = job.y - w + 1;
   auto slot = [&](int k) -> const float* {
     return a.part + ((size_t)(w + k) * 2 + (k == 0 ? 1 : 0)) * SH::PSZ;
   };
-  const int K = job.y - w + 1;
+  constexpr int KB = 8;  // partials fetched per batch
   float M = -INFINITY;
-  for (int k = 0; k < K; ++k) M = fmaxf(M, slot(k)[G * D + g]);
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    float mk[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) mk[k] = k0 + k < K ? slot(k0 + k)[G * D + g] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) M = fmaxf(M, mk[k]);
+  }
   float res[OPL];
 #pragma unroll
   for (int i = 0; i < OPL; ++i) res[i] = 0.f;
   float lt = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const float* p = slot(k);
-    const float mk = p[G * D + g];
-    const float wk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-    lt = fmaf(wk, p[G * D + G + g], lt);
+  constexpr int KD = 4;
+  for (int k0 = 0; k0 < K; k0 += KD) {
+    float x[KD][OPL], mk[KD], lk[KD];
 #pragma unroll
-    for (int i = 0; i < OPL; ++i) res[i] = fmaf(wk, p[o0 + i], res[i]);
+    for (int k = 0; k < KD; ++k) {
+      if (k0 + k < K) {
+        const float* p = slot(k0 + k);
+        mk[k] = p[G * D + g];
+        lk[k] = p[G * D + G + g];
+        if constexpr (OPL % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < OPL; i += 4) {
+            const float4 v = *(const float4*)(p + o0 + i);
+            x[k][i] = v.x; x[k][i + 1] = v.y; x[k][i + 2] = v.z; x[k][i + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < OPL; ++i) x[k][i] = p[o0 + i];
+        }
+      } else {
+        mk[k] = -INFINITY;
+        lk[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < OPL; ++i) x[k][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      const float wk = (mk[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+      lt = fmaf(wk, lk[k], lt);
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) res[i] = fmaf(wk, x[k][i], res[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < OPL; ++i) res[i] = res[i] / lt;
@@ -546,7 +650,6 @@ static DecodeKernels kernels_for() {
   using SH = DShape<T, D, G>;
   return {(const void*)decode_main<T, D, G>, (const void*)decode_merge<T, D, G>, SH::NT, SH::PSZ};
 }
-
 static bool pick(int dtype, int D, int G, DecodeKernels* k) {
 #define PKV_CASE(TT, DD, GG)                      \
   if (D == DD && G == GG) {                       \
@@ -573,17 +676,18 @@ bool decode_supported(int dtype, int head_dim, int group) {
   return pick(dtype, head_dim, group, &k);
 }
 
-// Number of wavefronts of the persistent grid: every resident slot of the
-// device (bounded by a tuning cap), never more than the chunks there can be.
+// Number of wavefronts of the persistent grid: a fixed number of
+// workgroups per compute unit (PKV_DECODE_WG_PER_CU overrides the device's
+// occupancy limit), never more than the chunks there can be.
 static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B) {
   const DeviceInfo& dev = device_info();
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 64 * kWavesPerWG, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  const int cap = tuning_int("PKV_DECODE_WG_PER_CU", 0);
-  if (cap > 0) per_cu = std::min(per_cu, cap);
-  long long wgs = (long long)per_cu * dev.num_cus;
+  const int force = tuning_int("PKV_DECODE_WG_PER_CU", 0);
+  if (force > 0) per_cu = std::min(force, 8);
+  long long wgs = (long long)per_cu * std::max(dev.num_cus, 1);
   const long long maxctx = (long long)max_blocks * B;
   const long long upper = (long long)Hkv * S * ((maxctx + k.nt - 1) / k.nt);
   long long need_wg = (upper + kWavesPerWG - 1) / kWavesPerWG;
@@ -593,12 +697,19 @@ static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, 
   return (int)(wgs * kWavesPerWG);
 }
 
+// Workspace: two partial slots per wavefront, then one job entry per
+// wavefront.
+static size_t workspace_layout(const DecodeKernels& k, int nW, size_t* jobs_off) {
+  const size_t part = (size_t)nW * 2 * k.psz * sizeof(float);
+  *jobs_off = ((part + 255) / 256) * 256;
+  return *jobs_off + (size_t)nW * sizeof(int2);
+}
+
 size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_blocks, int B) {
   DecodeKernels k;
   if (!pick(dtype, D, G, &k)) return 0;
-  const int nW = decode_waves(k, S, Hkv, max_blocks, B);
-  const size_t part = (size_t)nW * 2 * k.psz * sizeof(float);
-  return ((part + 255) / 256) * 256 + (size_t)nW * sizeof(int2);
+  size_t off;
+  return workspace_layout(k, decode_waves(k, S, Hkv, max_blocks, B), &off);
 }
 
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
@@ -607,8 +718,8 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   DecodeKernels k;
   if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
   const int nW = decode_waves(k, S, Hkv, max_blocks, B);
-  const size_t part = (size_t)nW * 2 * k.psz * sizeof(float);
-  const size_t need = ((part + 255) / 256) * 256 + (size_t)nW * sizeof(int2);
+  size_t jobs_off;
+  const size_t need = workspace_layout(k, nW, &jobs_off);
   if (ws == nullptr || ws_bytes < need) return -7;
   DecodeArgs a;
   a.out = out;
@@ -618,7 +729,7 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.tables = tables;
   a.ctx_lens = ctx;
   a.part = (float*)ws;
-  a.jobs = (int2*)((char*)ws + ((part + 255) / 256) * 256);
+  a.jobs = (int2*)((char*)ws + jobs_off);
   a.S = S;
   a.Hq = Hq;
   a.Hkv = Hkv;

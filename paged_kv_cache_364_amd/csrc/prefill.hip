@@ -1,14 +1,351 @@
-// Paged prefill attention (MFMA path): not built yet in this revision.
+// Paged prefill attention for gfx950 on the matrix cores.
+//
+// A chunk of C new query tokens per sequence attends, causally, to the
+// sequence's cached prefix plus the chunk itself, all read through the
+// block table (cnblogs "paged attention", section 5: position -> logical
+// block -> physical block).  Scores are computed block-wise and partial
+// results are merged as they go (intelliparadigm.com article, section 2.2),
+// here with the running-max online softmax, so the result is the plain
+// softmax(scale * Q K^T) V of the pages (cnblogs section 6).
+//
+// Tiling.  A workgroup of four wavefronts owns BM = 128 query rows of one
+// (sequence, head); wavefront w owns rows 32w .. 32w + 31.  Keys and values
+// are walked in tiles of KT = 64 tokens (several physical blocks gathered
+// through the table), double-buffered in LDS: the global loads of tile j + 1
+// are in flight while tile j is computed.  Per tile and wavefront:
+//
+//   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = the
+//                 wavefront's query rows, held in registers for the whole
+//                 loop.  The accumulator layout puts query l % 32 on lane l
+//                 and 16 keys in its registers, so the online-softmax state
+//                 (running max, running sum) of a query lives in one lane
+//                 pair (l, l ^ 32).
+//   O^T += V^T P^T  A = V^T from LDS, B = P^T taken straight from the S^T
+//                 accumulators (converted to bf16): the keys a lane holds
+//                 in registers are exactly the contraction index the B
+//                 operand wants, provided V^T stores each 16-key group in
+//                 the order of that register layout.  V is written to LDS
+//                 transposed, in that order.
+//
+// A matrix-core contraction sums over its k index in any order, so the
+// assignment of keys (for O^T) or head dimensions (for S^T) to registers
+// only has to agree between the two operands; rows and columns follow the
+// documented 32x32 accumulator layout (lane l holds column l % 32 and rows
+// 8 * (r / 4) + 4 * (l / 32) + r % 4 of register r).
 #include "common.h"
 #include "kernels.h"
 
 namespace pkv {
 
-bool prefill_supported(int, int, int, int) { return false; }
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-int launch_prefill(void*, const void*, const int32_t*, int, int, const void*, const void*, const int32_t*, int,
-                   const int32_t*, int, int, int, int, int, int, float, hipStream_t) {
-  return -2;
+struct PrefillArgs {
+  uint16_t* out;
+  const uint16_t* q;
+  const int32_t* cu_q_lens;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  int S, Hq, Hkv, G, max_blocks, num_blocks, log2B, q_tiles;
+  float scale_log2;
+};
+
+constexpr int kPBM = 128;  // query rows per workgroup
+constexpr int kPKT = 64;   // keys per tile
+constexpr int kPThreads = 256;
+
+template <int D>
+struct PShape {
+  static constexpr int KS = D / 16;          // contraction steps of S^T
+  static constexpr int DT = D / 32;          // 32-row tiles of O^T
+  static constexpr int PIECES = D / 8;       // 16-byte pieces per row
+  static constexpr int KROW = D + 8;         // K row in LDS (bf16), padded
+  static constexpr int VROW = kPKT + 8;      // V^T row in LDS (bf16), padded
+  static constexpr int K_ELEMS = kPKT * KROW;
+  static constexpr int V_ELEMS = D * VROW;
+  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int K_LOADS = kPKT * PIECES / kPThreads;        // 16-byte K pieces per thread
+  static constexpr int V_PAIRS = (kPKT / 2) * PIECES / kPThreads;  // (2 keys x 16 bytes) V pieces per thread
+  static_assert(K_LOADS >= 1 && V_PAIRS >= 1, "head_dim too small for the tile");
+};
+
+// Position of key u (0..63) inside its 16-key group of a V^T row: the order
+// in which the S^T accumulator registers of a lane pair hold those keys.
+__device__ __forceinline__ int vt_pos(int u) {
+  const int v = u & 15;
+  return (u & ~15) + 8 * ((v >> 2) & 1) + 4 * (v >> 3) + (v & 3);
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) { return pack_bf16x2(a, b); }
+
+template <int D>
+struct TileRegs {
+  uint4 k[PShape<D>::K_LOADS];
+  uint4 v0[PShape<D>::V_PAIRS];
+  uint4 v1[PShape<D>::V_PAIRS];
+};
+
+// Physical row (in elements) of absolute key t of the sequence, or -1 past
+// the context, or -2 for a block id outside the pool.
+__device__ __forceinline__ long long key_row(const PrefillArgs& a, const int32_t* trow, int kvh, int t, int ctx) {
+  if (t >= ctx) return -1;
+  const int blk = trow[t >> a.log2B];
+  if ((unsigned)blk >= (unsigned)a.num_blocks) return -2;
+  return (((long long)blk * a.Hkv + kvh) << a.log2B) + (t & ((1 << a.log2B) - 1));
+}
+
+__device__ __forceinline__ uint4 load_row_piece(const uint16_t* base, long long row, int D, int piece) {
+  if (row >= 0) return *(const uint4*)(base + row * D + piece * 8);
+  if (row == -2) return make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);  // NaN
+  return make_uint4(0, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int32_t* trow, int kvh,
+                                          int t0, int ctx, int tid) {
+  using PS = PShape<D>;
+#pragma unroll
+  for (int n = 0; n < PS::K_LOADS; ++n) {
+    const int idx = tid + n * kPThreads;
+    const int key = idx / PS::PIECES;
+    const int pc = idx % PS::PIECES;
+    r.k[n] = load_row_piece(a.k_cache, key_row(a, trow, kvh, t0 + key, ctx), D, pc);
+  }
+#pragma unroll
+  for (int n = 0; n < PS::V_PAIRS; ++n) {
+    const int idx = tid + n * kPThreads;
+    const int pair = idx % (kPKT / 2);
+    const int pc = idx / (kPKT / 2);
+    r.v0[n] = load_row_piece(a.v_cache, key_row(a, trow, kvh, t0 + 2 * pair, ctx), D, pc);
+    r.v1[n] = load_row_piece(a.v_cache, key_row(a, trow, kvh, t0 + 2 * pair + 1, ctx), D, pc);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, int tid) {
+  using PS = PShape<D>;
+  uint16_t* kl = buf;
+  uint16_t* vl = buf + PS::K_ELEMS;
+#pragma unroll
+  for (int n = 0; n < PS::K_LOADS; ++n) {
+    const int idx = tid + n * kPThreads;
+    const int key = idx / PS::PIECES;
+    const int pc = idx % PS::PIECES;
+    *(uint4*)(kl + key * PS::KROW + pc * 8) = r.k[n];
+  }
+#pragma unroll
+  for (int n = 0; n < PS::V_PAIRS; ++n) {
+    const int idx = tid + n * kPThreads;
+    const int pair = idx % (kPKT / 2);
+    const int pc = idx / (kPKT / 2);
+    const int pos = vt_pos(2 * pair);  // even; key 2 * pair + 1 sits next to it
+    const uint32_t a0[4] = {r.v0[n].x, r.v0[n].y, r.v0[n].z, r.v0[n].w};
+    const uint32_t a1[4] = {r.v1[n].x, r.v1[n].y, r.v1[n].z, r.v1[n].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = (a0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t hi = (a1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      *(uint32_t*)(vl + (pc * 8 + e) * PS::VROW + pos) = lo | (hi << 16);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+  using PS = PShape<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PS::BUF_ELEMS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;  // lane half
+  const int lq = lane & 31;
+
+  // Workgroup -> (unit, q tile).  Workgroups are dealt to the 8 XCDs round
+  // robin; all q tiles of one (sequence, head) go to one XCD, one after the
+  // other and heaviest (last) first, so they share its L2 for the keys and
+  // values, and consecutive units spread over the XCDs.
+  const int f = blockIdx.x;
+  const int xcd = f & 7;
+  const int k = f >> 3;
+  const int unit = (k / a.q_tiles) * 8 + xcd;
+  const int qt = a.q_tiles - 1 - (k % a.q_tiles);
+  if (unit >= a.S * a.Hq) return;
+  const int s = unit / a.Hq;
+  const int h = unit - s * a.Hq;
+  const int kvh = h / a.G;
+  const int qbeg = a.cu_q_lens[s];
+  const int C = a.cu_q_lens[s + 1] - qbeg;
+  const int q0 = qt * kPBM;
+  if (q0 >= C) return;
+  const int ctx = min(a.ctx_lens[s], a.max_blocks << a.log2B);  // never past the table
+  const int P = ctx - C;  // cached prefix length
+  const int rows_end = min(C, q0 + kPBM);
+  const int n_tiles = (P + rows_end - 1) / kPKT + 1;  // keys 0 .. P + rows_end - 1
+  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+
+  // this wavefront's query rows and their B operands (query l % 32)
+  const int wr0 = q0 + wave * 32;
+  const bool wave_live = wr0 < C;
+  const int my_row = wr0 + lq;
+  const bool row_ok = my_row < C;
+  const int my_pos = P + my_row;
+  const int wave_last_pos = P + min(wr0 + 31, C - 1);
+  bf16x8_t qreg[PS::KS];
+  {
+    const uint16_t* qp = a.q + ((size_t)(qbeg + min(my_row, C - 1)) * a.Hq + h) * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < PS::KS; ++ks) {
+      const uint4 v = row_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x16_t acc_o[PS::DT];
+#pragma unroll
+  for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  TileRegs<D> tr;
+  load_tile<D>(tr, a, trow, kvh, 0, ctx, tid);
+  store_tile<D>(tr, lds, tid);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const uint16_t* buf = lds + (j & 1) * PS::BUF_ELEMS;
+    if (j + 1 < n_tiles) load_tile<D>(tr, a, trow, kvh, (j + 1) * kPKT, ctx, tid);
+    const int t0 = j * kPKT;
+    if (wave_live && t0 <= wave_last_pos) {
+      const uint16_t* kl = buf;
+      const uint16_t* vl = buf + PS::K_ELEMS;
+      // S^T for keys t0 .. t0 + 63 (two 32-key tiles) x this wave's 32 queries
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+        const uint16_t* krow = kl + (mt * 32 + lq) * PS::KROW + hh * 8;
+#pragma unroll
+        for (int ks = 0; ks < PS::KS; ++ks) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + ks * 16));
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[mt], 0, 0, 0);
+        }
+      }
+      // scale, causal / context mask, tile max
+      const bool need_mask = (t0 + kPKT - 1 > P + wr0) || (t0 + kPKT > ctx);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[mt][r] * a.scale_log2;
+          if (need_mask) {
+            const int t = t0 + mt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (t > my_pos || t >= ctx) x = -INFINITY;
+          }
+          sacc[mt][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      float psum = 0.f;
+      // P^T in bf16, grouped by 16-key contraction steps
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[kk >> 1][8 * (kk & 1) + e] - msub);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[kk >> 1][8 * (kk & 1) + e + 1] - msub);
+          psum += p0 + p1;
+          w4[e >> 1] = pack2_bf16(p0, p1);
+        }
+        pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int dt = 0; dt < PS::DT; ++dt) {
+        const uint16_t* vrow = vl + (dt * 32 + lq) * PS::VROW + hh * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const uint4*)(vrow + kk * 16));
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], acc_o[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (j + 1 < n_tiles) store_tile<D>(tr, lds + ((j + 1) & 1) * PS::BUF_ELEMS, tid);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* op = a.out + ((size_t)(qbeg + my_row) * a.Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = dt * 32 + 8 * rq + 4 * hh;
+      const uint2 v = make_uint2(pack2_bf16(acc_o[dt][4 * rq] * inv, acc_o[dt][4 * rq + 1] * inv),
+                                 pack2_bf16(acc_o[dt][4 * rq + 2] * inv, acc_o[dt][4 * rq + 3] * inv));
+      *(uint2*)(op + d0) = v;
+    }
+}
+
+bool prefill_supported(int dtype, int head_dim, int group, int block_size) {
+  (void)group;
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && block_size >= 1 && block_size <= 64 &&
+         (block_size & (block_size - 1)) == 0;
+}
+
+int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                   const void* k_cache, const void* v_cache, const int32_t* tables, int max_blocks,
+                   const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks, float scale,
+                   hipStream_t stream) {
+  (void)total_q;
+  PrefillArgs a;
+  a.out = (uint16_t*)out;
+  a.q = (const uint16_t*)q;
+  a.cu_q_lens = cu_q_lens;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.tables = tables;
+  a.ctx_lens = ctx;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.log2B = 0;
+  while ((1 << a.log2B) < B) ++a.log2B;
+  a.q_tiles = (max_q_len + kPBM - 1) / kPBM;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const long long units = (long long)S * Hq;
+  const long long grid = (units + 7) / 8 * 8 * a.q_tiles;
+  if (grid <= 0) return 0;
+  if (grid > 0x7fffffffLL) return -2;
+  if (D == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, a);
+  else if (D == 64)
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, a);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 }  // namespace pkv

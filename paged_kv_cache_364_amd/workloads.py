@@ -318,7 +318,7 @@ def config4():
 
 
 def prefill_workload(seed=5, num_seqs=16, prefix_hi=1536, chunk=512, num_blocks=4096,
-                     heads=OPT13B, name=None, prefix_lens=None, chunk_lens=None):
+                     heads=OPT13B, name=None, prefix_lens=None, chunk_lens=None, block_size=16):
     """Paged prefill: each sequence has a cached prefix P ~ U{0..prefix_hi}
     and a new causal query chunk of ``chunk`` tokens whose K/V are written
     first; the chunk then attends over prefix + chunk."""
@@ -352,10 +352,10 @@ def prefill_workload(seed=5, num_seqs=16, prefix_hi=1536, chunk=512, num_blocks=
         if n:
             b.ops.append(Op("append", s, n=n, k=kc[off: off + n], v=vc[off: off + n]))
         off += n
-    mb = -(-(int(pl.max()) + max(cl)) // 16) if num_seqs else 1
-    return Workload(name or f"opt13b-prefill-b{num_seqs}x{chunk}", "prefill", BF16, hq, hkv, d, 16,
+    mb = max(-(-(int(p) + c) // block_size) for p, c in zip(pl, cl)) if num_seqs else 1
+    return Workload(name or f"opt13b-prefill-b{num_seqs}x{chunk}", "prefill", BF16, hq, hkv, d, block_size,
                     num_blocks, _scale(d), init_order, [a, b], list(range(num_seqs)), q,
-                    q_lens=cl, max_blocks_per_seq=mb)
+                    q_lens=cl, max_blocks_per_seq=max(mb, 1))
 
 
 def config5():

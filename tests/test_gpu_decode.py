@@ -223,3 +223,29 @@ def test_workspace_too_small_is_rejected():
         api.paged_attention_decode(torch.empty_like(q), q, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev,
                                    float(wl.scale), workspace=ws)
     assert e.value.status == PKV_ERR_WORKSPACE
+
+
+def test_workspace_reused_across_calls_and_garbage_filled():
+    """Split units are merged by the wavefront that arrives last; its arrival
+    counters live in the caller's workspace and carry a per-call epoch, so a
+    workspace reused by many calls, or filled with garbage, gives the same
+    results."""
+    wl_a = W.llama_decode(21, 24, 100, 3000, 8192, "llama-ws-a")
+    wl_b = W.llama_decode(22, 40, 1, 2048, 8192, "llama-ws-b")
+    st_a, st_b = driver.run_script(wl_a), driver.run_script(wl_b)
+    exp_a = oracle_runner.expected(wl_a, oracle_runner.run(wl_a))
+    exp_b = oracle_runner.expected(wl_b, oracle_runner.run(wl_b))
+    n = max(api.decode_workspace_size(len(w.batch), 32, 8, 128, 16, w.max_blocks_per_seq, torch.bfloat16)
+            for w in (wl_a, wl_b))
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    first = None
+    for i in range(6):
+        wl, st, exp = (wl_a, st_a, exp_a) if i % 2 == 0 else (wl_b, st_b, exp_b)
+        out = driver.run_attention(wl, st, workspace=ws)
+        torch.cuda.synchronize()
+        got = driver.out_to_f64(out)
+        compare(wl, got, exp)
+        if i == 0:
+            first = got
+        elif i % 2 == 0:
+            assert np.array_equal(got, first), "repeated call differs"
