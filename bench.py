@@ -1,14 +1,22 @@
-"""Paged decode attention benchmark (Llama-3.1-8B attention shape).
+"""Paged decode attention benchmark (Llama-3.1-8B attention shape), with a
+paged prefill leg (OPT-13B shape).
 
-One step = the device work of one decode step for one layer of the batch:
-``kv_write`` of the batch's new tokens into their slots, then
+Decode step = the device work of one decode step of one layer for the whole
+batch: ``kv_write`` of the 64 new tokens into their slots, then
 ``paged_attention_decode`` (main pass + log-sum-exp merge) over the paged
-cache.  Layers rotate over separate per-layer pools (32 x 25,600 blocks,
-50 GiB in all) so the 256 MB Infinity Cache cannot hold the working set.
+cache.  Block tables and slot mappings come from the C++ block allocator and
+are resident on the device before timing starts.  Layers rotate over
+separate per-layer pools (32 x 25,600 blocks = 50 GiB) so the 256 MB
+Infinity Cache cannot hold the working set.
 
-Prints one JSON line.  ``value`` is KV bytes the attention must read per
-step (sum of context lengths x kv heads x head_dim x 2 tensors x 2 bytes)
-divided by the measured time per step.
+``value`` = KV bytes the attention must read per step (sum of context
+lengths x kv heads x head_dim x 2 tensors x 2 bytes) / wall time per step.
+
+Prefill leg: ``kv_write`` of the 16 x 512-token chunk, then
+``paged_attention_prefill`` over prefix + chunk (40 layers x 4,096 blocks
+rotated); reported in TFLOP/s of the causal attention's algorithmic flops.
+
+Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -23,11 +31,121 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
+# HBM bytes per dispatch from rocprofv3 counters (written by
+# paged_kv_cache_364_amd.profiling from two --pmc runs of this script)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama31_8b_b64_prefill_opt13b_b16x512.txt")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def timed_calls(torch, fn, n, warmup, stream):
+    """Average time per call (ms) of ``fn(i)`` from events recorded on the
+    stream the kernels run on, plus the list of per-call times."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return sum(ts) / len(ts), ts
+
+
+def copy_bandwidth(torch, api, dev, mib=2048):
+    """Bandwidth of a plain copy on this device: copy_blocks moving ``mib``
+    MiB (read) + ``mib`` MiB (write) between disjoint halves of a pool, each
+    call on fresh blocks so caches do not hold them.  GB/s of read+write."""
+    Hkv, B, D = 8, 16, 128
+    pair_bytes = 2 * Hkv * B * D * 2
+    n = mib * 1024 * 1024 // pair_bytes
+    rounds = 4
+    k = torch.empty((2 * n * rounds, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    k.view(torch.int16).fill_(1)
+    v.view(torch.int16).fill_(1)
+    pairs = []
+    for r in range(rounds):
+        base = 2 * n * r
+        pairs.append(torch.stack([torch.arange(base, base + n), torch.arange(base + n, base + 2 * n)], 1)
+                     .to(torch.int32).to(dev).contiguous())
+    stream = torch.cuda.current_stream()
+    avg, _ = timed_calls(torch, lambda i: api.copy_blocks(k, v, pairs[i % rounds]), rounds * 2, rounds, stream)
+    del k, v
+    torch.cuda.empty_cache()
+    return 2 * n * pair_bytes / (avg * 1e-3) / 1e9
+
+
+def prefill_leg(args, torch, np, api, driver, workloads, dev):
+    wl = workloads.config5()
+    st = driver.run_script(wl, device=dev)
+    torch.cuda.synchronize()
+    S, Hq, Hkv, D, B = len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    ctx = st.context_lens.astype(np.int64)
+    C = np.array(wl.q_lens, dtype=np.int64)
+    P = ctx - C
+    pairs = int((C * P + C * (C + 1) // 2).sum()) * Hq
+    flops = 4 * D * pairs
+    kv_bytes = int(ctx.sum()) * Hkv * D * 2 * 2
+    qo_bytes = 2 * int(C.sum()) * Hq * D * 2
+    L = max(1, args.prefill_layers)
+    kps, vps = [st.k_pool], [st.v_pool]
+    for _ in range(1, L):
+        kps.append(st.k_pool.clone())
+        vps.append(st.v_pool.clone())
+    q = driver.to_device(wl.q, wl.dtype, dev)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(driver.cu_lens(wl.q_lens)).to(dev)
+    chunk = wl.steps[-1]
+    kn = driver.to_device(np.concatenate([op.k for op in chunk.ops]), wl.dtype, dev)
+    vn = driver.to_device(np.concatenate([op.v for op in chunk.ops]), wl.dtype, dev)
+    slots = torch.tensor(st.step_slots[-1], dtype=torch.int32, device=dev)
+    scale = float(wl.scale)
+    stream = torch.cuda.current_stream()
+
+    def prefill(i):
+        li = i % L
+        api.paged_attention_prefill(out, q, cu, max(wl.q_lens), kps[li], vps[li], st.tables_dev, st.lens_dev, scale)
+
+    def write(i):
+        li = i % L
+        api.kv_write(kn, vn, slots, kps[li], vps[li])
+
+    pf_ms, pf_all = timed_calls(torch, prefill, args.prefill_steps, args.warmup, stream)
+    kw_ms, _ = timed_calls(torch, write, args.prefill_steps, args.warmup, stream)
+    tflops = flops / (pf_ms * 1e-3) / 1e12
+    log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
+        f"{kw_ms * 1e3:.1f} us")
+    traffic = None
+    try:
+        from paged_kv_cache_364_amd import profiling
+
+        tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE), ["prefill_kernel<128>"])
+        traffic = round(tb / 1e9, 4) if tb is not None else None
+    except Exception:
+        traffic = None
+    res = {
+        "workload": wl.name, "num_seqs": S, "chunk": int(C[0]), "prefix_lens": "uniform 0..1536 (seed 5)",
+        "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": B, "layers_rotated": L,
+        "prefill_us_avg": round(pf_ms * 1e3, 2),
+        "prefill_us_p10": round(float(np.percentile(pf_all, 10)) * 1e3, 2),
+        "prefill_us_p90": round(float(np.percentile(pf_all, 90)) * 1e3, 2),
+        "kv_write_chunk_us_avg": round(kw_ms * 1e3, 2),
+        "tflops": round(tflops, 2), "algorithmic_gflop": round(flops / 1e9, 3),
+        "min_hbm_bytes": kv_bytes + qo_bytes,
+        "hbm_gbps_at_min_bytes": round((kv_bytes + qo_bytes) / (pf_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128>", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+    }
+    del kps, vps
+    return res, (wl, st, out)
 
 
 def main():
@@ -36,6 +154,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--prefill-steps", type=int, default=40)
+    ap.add_argument("--prefill-layers", type=int, default=40)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-copy-bandwidth", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -43,13 +165,14 @@ def main():
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the kernels have no "
+                                   "multi-GPU path)"}))
         sys.exit(2)
 
     import numpy as np
     import torch
 
-    from paged_kv_cache_364_amd import api, driver, workloads
+    from paged_kv_cache_364_amd import api, driver, profiling, workloads
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -80,17 +203,7 @@ def main():
     ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
                      dtype=torch.uint8, device=dev)
     scale = float(wl.scale)
-
-    def step(i, ev=None):
-        li = i % L
-        if ev is not None:
-            ev[0].record()
-        api.kv_write(kn, vn, slots, kps[li], vps[li])
-        if ev is not None:
-            ev[1].record()
-        api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
-        if ev is not None:
-            ev[2].record()
+    stream = torch.cuda.current_stream()
 
     if args.calibrate_copy_mib > 0:
         # n source blocks -> n destination blocks of 64 KiB (K + V): n * 64 KiB read and written
@@ -104,10 +217,27 @@ def main():
         log(f"calibration copy: {n} block pairs, {2 * n * Hkv * B * D * 2} bytes read and written")
         del ck, cv
 
+    def decode(i):
+        li = i % L
+        api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
+
+    def step(i, ev=None):
+        li = i % L
+        if ev is not None:
+            ev[0].record(stream)
+        api.kv_write(kn, vn, slots, kps[li], vps[li])
+        if ev is not None:
+            ev[1].record(stream)
+        api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
+    # timed region: K whole steps, wall clock between two synchronisations;
+    # per-kernel events ride along on the kernels' stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -122,11 +252,14 @@ def main():
     log(f"decode avg {dec_avg * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); kv_write avg {kvw_ms.mean() * 1e3:.1f} us; "
         f"wall {ms_per_step * 1e3:.1f} us/step")
+    # decode alone, back to back (no kv_write between calls)
+    dec_only_ms, _ = timed_calls(torch, decode, K, 5, stream)
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = (kv_bytes + qo_bytes) / (dec_avg * 1e-3) / 1e9
+    tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE),
+                                 ["decode_main<bf16_t, 128, 4>", "decode_merge<bf16_t, 128, 4>"])
 
-    # parity of the last output (layer data are identical copies of layer 0)
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seqs/s/layer, Llama-3.1-8B shape",
         "value": round(value, 2),
@@ -143,23 +276,39 @@ def main():
         "config": {"workload": wl.name, "num_seqs": S, "context_lens": "uniform 128..2048 (seed 2)",
                    "sum_context": sum_ctx, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "pool_blocks_per_layer": wl.num_blocks, "layers_rotated": L,
-                   "parallelism": "single GPU"},
+                   "step": "kv_write + paged_attention_decode, one layer", "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
         "decode_us_avg": round(dec_avg * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+        "decode_only_us_avg": round(dec_only_ms * 1e3, 2),
         "kv_write_us_avg": round(float(kvw_ms.mean()) * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (decode_main + decode_merge)",
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode = decode_main + decode_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": round(tb / 1e9, 4) if tb is not None else None},
     }
+    got_decode = driver.out_to_f64(out)
+    del kps, vps
+    torch.cuda.empty_cache()
+
+    if not args.no_copy_bandwidth:
+        cbw = copy_bandwidth(torch, api, dev)
+        result["copy_kernel_gbps"] = round(cbw, 1)
+        result["roofline"]["frac_of_copy_kernel"] = round(achieved / cbw, 4)
+        log(f"copy_blocks bandwidth (read + write) {cbw:.0f} GB/s")
+
+    pf = None
+    if not args.no_prefill:
+        pf, pf_state = prefill_leg(args, torch, np, api, driver, workloads, dev)
+        result["prefill"] = pf
 
     if not args.no_cpu_baseline:
         from oracle import runner as oracle_runner
 
         ost = oracle_runner.run(wl)
-        got = driver.out_to_f64(out)
         runs, t_cpu = 0, 0.0
         exp = None
         while runs == 0 or t_cpu < args.cpu_baseline_seconds:
@@ -167,7 +316,7 @@ def main():
             exp = oracle_runner.expected(wl, ost)
             t_cpu += time.perf_counter() - t1
             runs += 1
-        err = float(np.abs(got - exp).max())
+        err = float(np.abs(got_decode - exp).max())
         try:
             from threadpoolctl import threadpool_info
             cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -176,10 +325,19 @@ def main():
         result["cpu_baseline"] = {
             "value": round(kv_bytes * runs / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"full {wl.name} batch (layer 0), {runs} runs, {t_cpu:.1f}s; numpy fp64 on "
-                      f"{platform.processor() or platform.machine()}, os.cpu_count={os.cpu_count()}"}
+            "sample": f"the full {wl.name} batch (layer 0, {sum_ctx} context tokens) {runs} times in "
+                      f"{t_cpu:.1f}s; numpy float64 on {platform.machine()}, os.cpu_count={os.cpu_count()}, "
+                      f"BLAS threads={cores}"}
         result["parity_max_abs_err_vs_oracle"] = err
-        log(f"oracle {t_cpu / runs:.2f}s per batch, parity max abs err {err:.3g}")
+        log(f"oracle {t_cpu / runs:.2f}s per batch, decode parity max abs err {err:.3g}")
+        if pf is not None:
+            pwl, pst, pout = pf_state
+            post = oracle_runner.run(pwl)
+            t1 = time.perf_counter()
+            pexp = oracle_runner.expected(pwl, post)
+            pf["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+            pf["parity_max_abs_err_vs_oracle"] = float(np.abs(driver.out_to_f64(pout) - pexp).max())
+            log(f"prefill parity max abs err {pf['parity_max_abs_err_vs_oracle']:.3g}")
 
     print(json.dumps(result), flush=True)
 

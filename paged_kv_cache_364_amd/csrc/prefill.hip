@@ -55,6 +55,7 @@ struct PrefillArgs {
 constexpr int kPBM = 128;  // query rows per workgroup
 constexpr int kPKT = 64;   // keys per tile
 constexpr int kPThreads = 256;
+constexpr int kPTableLds = 1024;  // block-table entries staged in LDS per workgroup
 
 template <int D>
 struct PShape {
@@ -78,7 +79,15 @@ __device__ __forceinline__ int vt_pos(int u) {
   return (u & ~15) + 8 * ((v >> 2) & 1) + 4 * (v >> 3) + (v & 3);
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) { return pack_bf16x2(a, b); }
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v_t;
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  bf16x2v_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 template <int D>
 struct TileRegs {
@@ -88,10 +97,12 @@ struct TileRegs {
 };
 
 // Physical row (in elements) of absolute key t of the sequence, or -1 past
-// the context, or -2 for a block id outside the pool.
-__device__ __forceinline__ long long key_row(const PrefillArgs& a, const int32_t* trow, int kvh, int t, int ctx) {
+// the context, or -2 for a block id outside the pool.  Block ids come from
+// the workgroup's LDS window of the table: tbl[i] = entry tbase + i.
+__device__ __forceinline__ long long key_row(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t,
+                                             int ctx) {
   if (t >= ctx) return -1;
-  const int blk = trow[t >> a.log2B];
+  const int blk = tbl[(t >> a.log2B) - tbase];
   if ((unsigned)blk >= (unsigned)a.num_blocks) return -2;
   return (((long long)blk * a.Hkv + kvh) << a.log2B) + (t & ((1 << a.log2B) - 1));
 }
@@ -103,7 +114,7 @@ __device__ __forceinline__ uint4 load_row_piece(const uint16_t* base, long long 
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int32_t* trow, int kvh,
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int* tbl, int tbase, int kvh,
                                           int t0, int ctx, int tid) {
   using PS = PShape<D>;
 #pragma unroll
@@ -111,15 +122,15 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, 
     const int idx = tid + n * kPThreads;
     const int key = idx / PS::PIECES;
     const int pc = idx % PS::PIECES;
-    r.k[n] = load_row_piece(a.k_cache, key_row(a, trow, kvh, t0 + key, ctx), D, pc);
+    r.k[n] = load_row_piece(a.k_cache, key_row(a, tbl, tbase, kvh, t0 + key, ctx), D, pc);
   }
 #pragma unroll
   for (int n = 0; n < PS::V_PAIRS; ++n) {
     const int idx = tid + n * kPThreads;
     const int pair = idx % (kPKT / 2);
     const int pc = idx / (kPKT / 2);
-    r.v0[n] = load_row_piece(a.v_cache, key_row(a, trow, kvh, t0 + 2 * pair, ctx), D, pc);
-    r.v1[n] = load_row_piece(a.v_cache, key_row(a, trow, kvh, t0 + 2 * pair + 1, ctx), D, pc);
+    r.v0[n] = load_row_piece(a.v_cache, key_row(a, tbl, tbase, kvh, t0 + 2 * pair, ctx), D, pc);
+    r.v1[n] = load_row_piece(a.v_cache, key_row(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx), D, pc);
   }
 }
 
@@ -153,9 +164,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PS::BUF_ELEMS];
+  __shared__ int tbl[kPTableLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -209,14 +221,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Block-table window in LDS: entries tbase .. tbase + kPTableLds - 1 of
+  // the sequence's row (those the tiles need; keys past the causal limit
+  // are loaded too, then masked, so whole tiles must map to real blocks).
+  const int nblk_all = (min(ctx, n_tiles * kPKT) + (1 << a.log2B) - 1) >> a.log2B;
+  int tbase = 0;
+  auto fill_window = [&](int base) {
+    const int n = min(nblk_all - base, kPTableLds);
+    for (int i = tid; i < n; i += kPThreads) tbl[i] = trow[base + i];
+  };
+  fill_window(0);
+  __syncthreads();
+
   TileRegs<D> tr;
-  load_tile<D>(tr, a, trow, kvh, 0, ctx, tid);
+  load_tile<D>(tr, a, tbl, tbase, kvh, 0, ctx, tid);
   store_tile<D>(tr, lds, tid);
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const uint16_t* buf = lds + (j & 1) * PS::BUF_ELEMS;
-    if (j + 1 < n_tiles) load_tile<D>(tr, a, trow, kvh, (j + 1) * kPKT, ctx, tid);
+    if (j + 1 < n_tiles) {
+      // slide the window when tile j + 1 leaves it (uniform over the workgroup)
+      const int last_blk = (min((j + 2) * kPKT, ctx) - 1) >> a.log2B;
+      if (last_blk >= tbase + kPTableLds) {
+        __syncthreads();
+        tbase = ((j + 1) * kPKT) >> a.log2B;
+        fill_window(tbase);
+        __syncthreads();
+      }
+      load_tile<D>(tr, a, tbl, tbase, kvh, (j + 1) * kPKT, ctx, tid);
+    }
     const int t0 = j * kPKT;
     if (wave_live && t0 <= wave_last_pos) {
       const uint16_t* kl = buf;

@@ -1,0 +1,151 @@
+"""Summaries of rocprofv3 output for the kernels of libpagedkv.so.
+
+``python -m paged_kv_cache_364_amd.profiling stats DIR OUT.txt CMD...``
+    writes the per-kernel duration table of a ``--kernel-trace --stats``
+    run (``*_kernel_stats.csv`` under DIR) to OUT.txt, headed by CMD.
+
+``python -m paged_kv_cache_364_amd.profiling traffic FETCH_DIR WRITE_DIR CAL_BYTES OUT.txt CMD...``
+    reads two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
+    benchmark with ``--calibrate-copy-mib`` set, scales each counter by what
+    it reads for the calibration copy (the run's one copy_blocks dispatch,
+    which reads and writes CAL_BYTES bytes), and writes per-dispatch HBM bytes of every kernel of this
+    library, plus a JSON line that ``bench.py`` reads back.  The JSON carries
+    the SHA-256 of the kernel sources, so a figure taken before a kernel
+    changed is not reported for the new one.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+from typing import Dict, List
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "decode": ["csrc/decode.hip", "csrc/common.h"],
+    "prefill": ["csrc/prefill.hip", "csrc/common.h"],
+    "cache_ops": ["csrc/cache_ops.hip", "csrc/common.h"],
+}
+KIB = 1024
+
+
+def sources_sha(group: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[group]:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_group(name: str) -> str:
+    if "decode_" in name:
+        return "decode"
+    if "prefill_" in name:
+        return "prefill"
+    if "kv_write" in name or "copy_blocks" in name:
+        return "cache_ops"
+    return ""
+
+
+def short(name: str) -> str:
+    n = name.split("(")[0]
+    return n.replace("void ", "").replace("pkv::", "")
+
+
+def _one(pattern: str) -> str:
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise FileNotFoundError(pattern)
+    return files[0]
+
+
+def stats_summary(d: str, out: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    lines = [f"# rocprofv3 kernel statistics", f"command: {cmd}", "",
+             f"{'kernel':70s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}"]
+    for r in rows:
+        lines.append(f"{short(r['Name'])[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _pmc(d: str, counter: str) -> List[dict]:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    return [r for r in rows if r["Counter_Name"] == counter]
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, cal_bytes: int, out: str, cmd: str) -> Dict:
+    fetch, write = _pmc(fetch_dir, "FETCH_SIZE"), _pmc(write_dir, "WRITE_SIZE")
+    # calibration: the one copy_blocks dispatch moves a known byte count; the
+    # benchmark prints it, and it is the only copy_blocks launch in the run
+    cal_f = [float(r["Counter_Value"]) for r in fetch if "copy_blocks" in r["Kernel_Name"]]
+    cal_w = [float(r["Counter_Value"]) for r in write if "copy_blocks" in r["Kernel_Name"]]
+    if len(cal_f) != 1 or len(cal_w) != 1:
+        raise RuntimeError("expected exactly one calibration copy_blocks dispatch per run")
+    scale_f = cal_bytes / (cal_f[0] * KIB)
+    scale_w = cal_bytes / (cal_w[0] * KIB)
+    per: Dict[str, Dict[str, List[float]]] = {}
+    for rows, key in ((fetch, "fetch"), (write, "write")):
+        for r in rows:
+            g = kernel_group(r["Kernel_Name"])
+            if not g or "copy_blocks" in r["Kernel_Name"]:
+                continue
+            per.setdefault(short(r["Kernel_Name"]), {"fetch": [], "write": []})[key].append(
+                float(r["Counter_Value"]))
+    result = {"scale_fetch": scale_f, "scale_write": scale_w, "calibration_bytes": cal_bytes, "kernels": {}}
+    lines = ["# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", f"command: {cmd}", "",
+             f"calibration: copy_blocks moved {cal_bytes} bytes each way; FETCH_SIZE read "
+             f"{cal_f[0]:.1f} KiB (scale {scale_f:.4f}), WRITE_SIZE read {cal_w[0]:.1f} KiB "
+             f"(scale {scale_w:.4f})", "",
+             f"{'kernel':60s} {'n':>3s} {'fetch KiB':>12s} {'write KiB':>12s} {'scaled MB':>11s}"]
+    for name, v in per.items():
+        if not v["fetch"] or not v["write"]:
+            continue
+        fk, wk = statistics.median(v["fetch"]), statistics.median(v["write"])
+        mb = (fk * KIB * scale_f + wk * KIB * scale_w) / 1e6
+        g = kernel_group(name)
+        result["kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "bytes": mb * 1e6, "group": g,
+                                   "sources_sha256": sources_sha(g)}
+        lines.append(f"{name[:60]:60s} {len(v['fetch']):3d} {fk:12.1f} {wk:12.1f} {mb:11.2f}")
+    lines += ["", "json: " + json.dumps(result, sort_keys=True)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return result
+
+
+def read_traffic(path: str) -> Dict:
+    """The JSON line of a traffic summary, or {} when absent."""
+    if not os.path.exists(path):
+        return {}
+    for line in open(path):
+        if line.startswith("json: "):
+            return json.loads(line[6:])
+    return {}
+
+
+def traffic_bytes(summary: Dict, kernels: List[str]) -> float | None:
+    """Scaled HBM bytes per launch summed over ``kernels`` (short names), or
+    None if any is missing or its sources changed since it was measured."""
+    tot = 0.0
+    for k in kernels:
+        e = summary.get("kernels", {}).get(k)
+        if e is None or e.get("sources_sha256") != sources_sha(e["group"]):
+            return None
+        tot += e["bytes"]
+    return tot
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "stats":
+        stats_summary(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif mode == "traffic":
+        print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5],
+                                         " ".join(sys.argv[6:])), indent=1))
+    else:
+        raise SystemExit(__doc__)

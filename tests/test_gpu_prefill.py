@@ -69,6 +69,12 @@ def test_prefill_variants(hq, hkv, d, b):
     check(small(f"pf-{hq}-{hkv}-{d}-{b}", 60 + hq + d + b, [0, 5, 100, 63], [17, 64, 77, 129], hq, hkv, d, b))
 
 
+def test_prefill_table_window_slides():
+    """Block size 1 and contexts past 1024 blocks: the workgroup's LDS window
+    of the block table has to slide while the key tiles advance."""
+    check(small("pf-window", 91, [1100, 2500, 0], [50, 140, 1200], 4, 2, 64, 1))
+
+
 def test_prefill_opt13b_full():
     """16 sequences, prefix U{0..1536}, 512-token chunk, 40 heads, head_dim 128."""
     check(W.config5())
