@@ -8,11 +8,13 @@
 // here with the running-max online softmax, so the result is the plain
 // softmax(scale * Q K^T) V of the pages (cnblogs section 6).
 //
-// Tiling.  A workgroup of four wavefronts owns BM = 128 query rows of one
+// Tiling.  A workgroup of eight wavefronts owns BM = 256 query rows of one
 // (sequence, head); wavefront w owns rows 32w .. 32w + 31.  Keys and values
 // are walked in tiles of KT = 64 tokens (several physical blocks gathered
-// through the table), double-buffered in LDS: the global loads of tile j + 1
-// are in flight while tile j is computed.  Per tile and wavefront:
+// through the table), double-buffered in LDS and staged through two sets of
+// registers: the global loads of tile j + 2 are in flight while tile j is
+// computed.  The block-table entries the tiles need sit in an LDS window.
+// Per tile and wavefront:
 //
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = the
 //                 wavefront's query rows, held in registers for the whole
@@ -52,9 +54,10 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-constexpr int kPBM = 128;  // query rows per workgroup
-constexpr int kPKT = 64;   // keys per tile
-constexpr int kPThreads = 256;
+constexpr int kPWaves = 8;                 // wavefronts per workgroup, 32 query rows each
+constexpr int kPBM = 32 * kPWaves;         // query rows per workgroup
+constexpr int kPKT = 64;                   // keys per tile
+constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPTableLds = 1024;  // block-table entries staged in LDS per workgroup
 
 template <int D>
@@ -67,9 +70,10 @@ struct PShape {
   static constexpr int K_ELEMS = kPKT * KROW;
   static constexpr int V_ELEMS = D * VROW;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_LOADS = kPKT * PIECES / kPThreads;        // 16-byte K pieces per thread
-  static constexpr int V_PAIRS = (kPKT / 2) * PIECES / kPThreads;  // (2 keys x 16 bytes) V pieces per thread
-  static_assert(K_LOADS >= 1 && V_PAIRS >= 1, "head_dim too small for the tile");
+  static constexpr int K_TOTAL = kPKT * PIECES;                    // 16-byte K pieces per tile
+  static constexpr int V_TOTAL = (kPKT / 2) * PIECES;              // (2 keys x 16 bytes) V pieces per tile
+  static constexpr int K_LOADS = (K_TOTAL + kPThreads - 1) / kPThreads;  // per thread
+  static constexpr int V_PAIRS = (V_TOTAL + kPThreads - 1) / kPThreads;
 };
 
 // Position of key u (0..63) inside its 16-key group of a V^T row: the order
@@ -94,43 +98,68 @@ struct TileRegs {
   uint4 k[PShape<D>::K_LOADS];
   uint4 v0[PShape<D>::V_PAIRS];
   uint4 v1[PShape<D>::V_PAIRS];
+  uint32_t zero;  // bit per load: replace by zeros (key past the context)
+  uint32_t nan;   // bit per load: replace by NaN (block id outside the pool)
 };
 
-// Physical row (in elements) of absolute key t of the sequence, or -1 past
-// the context, or -2 for a block id outside the pool.  Block ids come from
-// the workgroup's LDS window of the table: tbl[i] = entry tbase + i.
-__device__ __forceinline__ long long key_row(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t,
-                                             int ctx) {
-  if (t >= ctx) return -1;
-  const int blk = tbl[(t >> a.log2B) - tbase];
-  if ((unsigned)blk >= (unsigned)a.num_blocks) return -2;
-  return (((long long)blk * a.Hkv + kvh) << a.log2B) + (t & ((1 << a.log2B) - 1));
+// Element offset of 16-byte piece `piece` of absolute key t of the sequence.
+// Every load is issued unconditionally from a valid address (block 0 when
+// the key has none) and flagged (code 1: key past the context, read as
+// zeros; code 2: block id outside the pool, read as NaN), so no branch sits
+// between a load and its use; the flags are applied when the tile is written
+// to LDS.  Block ids come from the workgroup's LDS window of the table:
+// tbl[i] = entry tbase + i.
+struct KeyPiece {
+  size_t off;
+  uint32_t code;
+};
+
+__device__ __forceinline__ KeyPiece key_piece(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t,
+                                              int ctx, int D, int piece) {
+  const bool in_ctx = t < ctx;
+  int blk = in_ctx ? tbl[(t >> a.log2B) - tbase] : 0;
+  const bool bad = in_ctx && (unsigned)blk >= (unsigned)a.num_blocks;
+  blk = bad ? 0 : blk;
+  const size_t row = (((size_t)blk * a.Hkv + kvh) << a.log2B) + (t & ((1 << a.log2B) - 1));
+  return {row * D + piece * 8, (in_ctx ? 0u : 1u) | (bad ? 2u : 0u)};
 }
 
-__device__ __forceinline__ uint4 load_row_piece(const uint16_t* base, long long row, int D, int piece) {
-  if (row >= 0) return *(const uint4*)(base + row * D + piece * 8);
-  if (row == -2) return make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);  // NaN
-  return make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ uint4 apply_fill(uint4 v, uint32_t zero, uint32_t nan, int bit) {
+  if ((zero >> bit) & 1) v = make_uint4(0, 0, 0, 0);
+  if ((nan >> bit) & 1) v = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+  return v;
 }
 
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int* tbl, int tbase, int kvh,
                                           int t0, int ctx, int tid) {
   using PS = PShape<D>;
+  r.zero = 0;
+  r.nan = 0;
 #pragma unroll
   for (int n = 0; n < PS::K_LOADS; ++n) {
     const int idx = tid + n * kPThreads;
+    if (PS::K_TOTAL % kPThreads != 0 && idx >= PS::K_TOTAL) break;
     const int key = idx / PS::PIECES;
     const int pc = idx % PS::PIECES;
-    r.k[n] = load_row_piece(a.k_cache, key_row(a, tbl, tbase, kvh, t0 + key, ctx), D, pc);
+    const KeyPiece kp = key_piece(a, tbl, tbase, kvh, t0 + key, ctx, D, pc);
+    r.k[n] = *(const uint4*)(a.k_cache + kp.off);
+    r.zero |= (kp.code & 1u) << n;
+    r.nan |= (kp.code >> 1) << n;
   }
 #pragma unroll
   for (int n = 0; n < PS::V_PAIRS; ++n) {
     const int idx = tid + n * kPThreads;
+    if (PS::V_TOTAL % kPThreads != 0 && idx >= PS::V_TOTAL) break;
     const int pair = idx % (kPKT / 2);
     const int pc = idx / (kPKT / 2);
-    r.v0[n] = load_row_piece(a.v_cache, key_row(a, tbl, tbase, kvh, t0 + 2 * pair, ctx), D, pc);
-    r.v1[n] = load_row_piece(a.v_cache, key_row(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx), D, pc);
+    const int b0 = PS::K_LOADS + 2 * n;
+    const KeyPiece p0 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair, ctx, D, pc);
+    const KeyPiece p1 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx, D, pc);
+    r.v0[n] = *(const uint4*)(a.v_cache + p0.off);
+    r.v1[n] = *(const uint4*)(a.v_cache + p1.off);
+    r.zero |= ((p0.code & 1u) << b0) | ((p1.code & 1u) << (b0 + 1));
+    r.nan |= ((p0.code >> 1) << b0) | ((p1.code >> 1) << (b0 + 1));
   }
 }
 
@@ -142,18 +171,23 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
 #pragma unroll
   for (int n = 0; n < PS::K_LOADS; ++n) {
     const int idx = tid + n * kPThreads;
+    if (PS::K_TOTAL % kPThreads != 0 && idx >= PS::K_TOTAL) break;
     const int key = idx / PS::PIECES;
     const int pc = idx % PS::PIECES;
-    *(uint4*)(kl + key * PS::KROW + pc * 8) = r.k[n];
+    *(uint4*)(kl + key * PS::KROW + pc * 8) = apply_fill(r.k[n], r.zero, r.nan, n);
   }
 #pragma unroll
   for (int n = 0; n < PS::V_PAIRS; ++n) {
     const int idx = tid + n * kPThreads;
+    if (PS::V_TOTAL % kPThreads != 0 && idx >= PS::V_TOTAL) break;
     const int pair = idx % (kPKT / 2);
     const int pc = idx / (kPKT / 2);
     const int pos = vt_pos(2 * pair);  // even; key 2 * pair + 1 sits next to it
-    const uint32_t a0[4] = {r.v0[n].x, r.v0[n].y, r.v0[n].z, r.v0[n].w};
-    const uint32_t a1[4] = {r.v1[n].x, r.v1[n].y, r.v1[n].z, r.v1[n].w};
+    const int b0 = PS::K_LOADS + 2 * n;
+    const uint4 x0 = apply_fill(r.v0[n], r.zero, r.nan, b0);
+    const uint4 x1 = apply_fill(r.v1[n], r.zero, r.nan, b0 + 1);
+    const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t lo = (a0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -164,7 +198,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PS::BUF_ELEMS];
   __shared__ int tbl[kPTableLds];
@@ -233,24 +267,23 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   fill_window(0);
   __syncthreads();
 
-  TileRegs<D> tr;
-  load_tile<D>(tr, a, tbl, tbase, kvh, 0, ctx, tid);
-  store_tile<D>(tr, lds, tid);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const uint16_t* buf = lds + (j & 1) * PS::BUF_ELEMS;
-    if (j + 1 < n_tiles) {
-      // slide the window when tile j + 1 leaves it (uniform over the workgroup)
-      const int last_blk = (min((j + 2) * kPKT, ctx) - 1) >> a.log2B;
-      if (last_blk >= tbase + kPTableLds) {
-        __syncthreads();
-        tbase = ((j + 1) * kPKT) >> a.log2B;
-        fill_window(tbase);
-        __syncthreads();
-      }
-      load_tile<D>(tr, a, tbl, tbase, kvh, (j + 1) * kPKT, ctx, tid);
+  // Key tiles flow global -> registers -> LDS.  Two register stages: while
+  // tile j is computed from LDS buffer j % 2, tile j + 1 (loaded one
+  // iteration earlier) waits in one stage and tile j + 2 loads into the
+  // other, so a tile's loads have a whole iteration to arrive.
+  auto load = [&](TileRegs<D>& r, int jt) {
+    // slide the window when tile jt leaves it (uniform over the workgroup)
+    const int last_blk = (min((jt + 1) * kPKT, ctx) - 1) >> a.log2B;
+    if (last_blk >= tbase + kPTableLds) {
+      __syncthreads();
+      tbase = (jt * kPKT) >> a.log2B;
+      fill_window(tbase);
+      __syncthreads();
     }
+    load_tile<D>(r, a, tbl, tbase, kvh, jt * kPKT, ctx, tid);
+  };
+  auto compute = [&](int j) {
+    const uint16_t* buf = lds + (j & 1) * PS::BUF_ELEMS;
     const int t0 = j * kPKT;
     if (wave_live && t0 <= wave_last_pos) {
       const uint16_t* kl = buf;
@@ -268,48 +301,78 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[mt], 0, 0, 0);
         }
       }
-      // scale, causal / context mask, tile max
+      // Scores in the log2 domain are c * s (c = scale * log2 e).  The tile
+      // max of a row is taken on the raw scores (c * max s, or c * min s
+      // for c < 0); masked keys (causal limit, context end) only occur in
+      // tiles on the diagonal or at the end, which take the select path.
+      const float c = a.scale_log2;
       const bool need_mask = (t0 + kPKT - 1 > P + wr0) || (t0 + kPKT > ctx);
-      float tmax = -INFINITY;
+      float tmax;
+      if (need_mask) {
+        tmax = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[mt][r] * a.scale_log2;
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int t = t0 + mt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (t > my_pos || t >= ctx) x = -INFINITY;
+            const float x = (t > my_pos || t >= ctx) ? -INFINITY : sacc[mt][r] * c;
+            sacc[mt][r] = x;
+            tmax = fmaxf(tmax, x);
           }
-          sacc[mt][r] = x;
-          tmax = fmaxf(tmax, x);
+      } else {
+        float hi = sacc[0][0], lo = sacc[0][0];
+        if (c >= 0.f) {
+#pragma unroll
+          for (int i = 1; i < 31; i += 2)
+            hi = __builtin_fmaxf(hi, __builtin_fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
+          hi = fmaxf(hi, sacc[1][15]);
+          tmax = c * hi;
+        } else {
+#pragma unroll
+          for (int i = 1; i < 31; i += 2)
+            lo = __builtin_fminf(lo, __builtin_fminf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
+          lo = fminf(lo, sacc[1][15]);
+          tmax = c * lo;
         }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      // Lazy running max: the reference m_run moves only when a score
+      // exceeds it by more than 2^8 (or on the first live tile), so the
+      // accumulators are rescaled rarely; weights stay below 256, well
+      // inside bf16 and fp32 range, and the final division by the row sum
+      // taken against the same reference cancels it exactly.
+      const bool move = tmax > m_run + 8.f;  // false while the row is all masked (tmax = -inf)
+      const float m_new = move ? tmax : m_run;
+      if (__ballot(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // exp2(-inf) = 0 at the start
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      }
+      m_run = m_new;
+      const float msub = (m_run == -INFINITY) ? 0.f : m_run;  // masked rows so far: weights 0
+      // P^T in bf16, grouped by 16-key contraction steps; the row sum adds
+      // the bf16 weights the matrix cores see (v_dot2 with ones)
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
       float psum = 0.f;
-      // P^T in bf16, grouped by 16-key contraction steps
       bf16x8_t pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint32_t w4[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[kk >> 1][8 * (kk & 1) + e] - msub);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[kk >> 1][8 * (kk & 1) + e + 1] - msub);
-          psum += p0 + p1;
+          const float x0 = sacc[kk >> 1][8 * (kk & 1) + e];
+          const float x1 = sacc[kk >> 1][8 * (kk & 1) + e + 1];
+          const float p0 = __builtin_amdgcn_exp2f(need_mask ? x0 - msub : __builtin_fmaf(x0, c, -msub));
+          const float p1 = __builtin_amdgcn_exp2f(need_mask ? x1 - msub : __builtin_fmaf(x1, c, -msub));
           w4[e >> 1] = pack2_bf16(p0, p1);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[e >> 1]), ones, psum, false);
         }
         pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int dt = 0; dt < PS::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      }
+      l_run += psum;
       // O^T += V^T P^T
 #pragma unroll
       for (int dt = 0; dt < PS::DT; ++dt) {
@@ -320,9 +383,26 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
           acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], acc_o[dt], 0, 0, 0);
         }
       }
-    }
-    if (j + 1 < n_tiles) store_tile<D>(tr, lds + ((j + 1) & 1) * PS::BUF_ELEMS, tid);
+        }
+  };
+  // one iteration: tile j + 1 waits in `ready`, `spare` receives tile j + 2
+  auto iteration = [&](int j, TileRegs<D>& ready, TileRegs<D>& spare) {
+    // issued every iteration (the last tile again near the end, unused) so
+    // that the wait for `ready` below never has to cover these loads
+    load(spare, min(j + 2, n_tiles - 1));
+    compute(j);
+    if (j + 1 < n_tiles) store_tile<D>(ready, lds + ((j + 1) & 1) * PS::BUF_ELEMS, tid);
     __syncthreads();
+  };
+
+  TileRegs<D> ra, rb;
+  load(ra, 0);
+  load(rb, min(1, n_tiles - 1));
+  store_tile<D>(ra, lds, tid);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    iteration(j, rb, ra);
+    if (j + 1 < n_tiles) iteration(j + 1, ra, rb);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
