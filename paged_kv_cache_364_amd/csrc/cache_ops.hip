@@ -28,14 +28,15 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const char* __restrict__ 
     const int rem = (int)(i - (long long)t * per_tok);
     const int h = rem / pieces_per_row;
     const int pc = rem - h * pieces_per_row;
+    // the row loads do not depend on the slot: issue all three together
+    const size_t src = ((size_t)t * Hkv + h) * rowb + (size_t)pc * 16;
+    const uint4 kx = *(const uint4*)(kn + src);
+    const uint4 vx = *(const uint4*)(vn + src);
     const int slot = slots[t];
     if (slot < 0 || slot >= total_slots) continue;
     const int blk = slot >> log2B;
     const int off = slot & ((1 << log2B) - 1);
     const size_t dst = ((((size_t)blk * Hkv + h) << log2B) + off) * rowb + (size_t)pc * 16;
-    const size_t src = ((size_t)t * Hkv + h) * rowb + (size_t)pc * 16;
-    const uint4 kx = *(const uint4*)(kn + src);
-    const uint4 vx = *(const uint4*)(vn + src);
     *(uint4*)(kc + dst) = kx;
     *(uint4*)(vc + dst) = vx;
   }

@@ -310,13 +310,18 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D, G>& ch, const ui
   const bool bad = (ch.bad >> jj) & 1;
   const float s = valid ? sc * scale_log2 : -INFINITY;
   const float cmax = group_max<SH::SH + ilog2(G), ilog2(LR), SH::FULL_ROWS>(s);
-  const float mnew = fmaxf(m, cmax);
-  const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+  // Lazy running max: the reference m moves only when the chunk's max
+  // exceeds it by more than 2^8 (or on the first valid chunk), so the
+  // accumulators are rescaled rarely; weights stay below 256 and the final
+  // division by the sum taken against the same reference cancels it.
+  const bool move = cmax > m + 8.f;  // m = -inf: moves on the first valid score
+  const float mnew = move ? cmax : m;
+  const float alpha = move ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
   const float p = valid ? __builtin_amdgcn_exp2f(s - mnew) : 0.f;
   lsum = lsum * alpha + p + (bad ? __builtin_nanf("") : 0.f);
   m = mnew;
-  // any head of any row group whose running max moved?
-  const bool rescale = __ballot(alpha != 1.f) != 0;
+  // any head of any row group whose reference moved?
+  const bool rescale = __ballot(move) != 0;
   if ((cl & ((1 << SH::SH) - 1)) == 0) {
     L[rg * NS + k] = p;
     if (k < G) L[SH::OFF_ALPHA + rg * G + k] = alpha;
@@ -583,24 +588,17 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   auto slot = [&](int k) -> const float* {
     return a.part + ((size_t)(w + k) * 2 + (k == 0 ? 1 : 0)) * SH::PSZ;
   };
-  constexpr int KB = 8;  // partials fetched per batch
-  float M = -INFINITY;
-  for (int k0 = 0; k0 < K; k0 += KB) {
-    float mk[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) mk[k] = k0 + k < K ? slot(k0 + k)[G * D + g] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < KB; ++k) M = fmaxf(M, mk[k]);
-  }
+  // Batches of KB partials: all loads of a batch are issued before any is
+  // used; the running max across batches rescales what was summed so far.
+  constexpr int KB = 8;
+  float M = -INFINITY, lt = 0.f;
   float res[OPL];
 #pragma unroll
   for (int i = 0; i < OPL; ++i) res[i] = 0.f;
-  float lt = 0.f;
-  constexpr int KD = 4;
-  for (int k0 = 0; k0 < K; k0 += KD) {
-    float x[KD][OPL], mk[KD], lk[KD];
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    float x[KB][OPL], mk[KB], lk[KB];
 #pragma unroll
-    for (int k = 0; k < KD; ++k) {
+    for (int k = 0; k < KB; ++k) {
       if (k0 + k < K) {
         const float* p = slot(k0 + k);
         mk[k] = p[G * D + g];
@@ -622,13 +620,21 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
         for (int i = 0; i < OPL; ++i) x[k][i] = 0.f;
       }
     }
+    float Mb = M;
 #pragma unroll
-    for (int k = 0; k < KD; ++k) {
-      const float wk = (mk[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+    for (int k = 0; k < KB; ++k) Mb = fmaxf(Mb, mk[k]);
+    const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+    lt *= r;
+#pragma unroll
+    for (int i = 0; i < OPL; ++i) res[i] *= r;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const float wk = (mk[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[k] - Mb);
       lt = fmaf(wk, lk[k], lt);
 #pragma unroll
       for (int i = 0; i < OPL; ++i) res[i] = fmaf(wk, x[k][i], res[i]);
     }
+    M = Mb;
   }
 #pragma unroll
   for (int i = 0; i < OPL; ++i) res[i] = res[i] / lt;
