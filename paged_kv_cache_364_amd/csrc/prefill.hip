@@ -288,17 +288,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     if (wave_live && t0 <= wave_last_pos) {
       const uint16_t* kl = buf;
       const uint16_t* vl = buf + PS::K_ELEMS;
-      // S^T for keys t0 .. t0 + 63 (two 32-key tiles) x this wave's 32 queries
+      // S^T for keys t0 .. t0 + 63 (two 32-key tiles) x this wave's 32
+      // queries.  The two accumulators alternate and the K fragments of
+      // the next contraction step are read while this step's products run.
       f32x16_t sacc[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-        const uint16_t* krow = kl + (mt * 32 + lq) * PS::KROW + hh * 8;
+      {
+        const uint16_t* k0 = kl + lq * PS::KROW + hh * 8;
+        const uint16_t* k1 = k0 + 32 * PS::KROW;
+        uint4 fa0 = *(const uint4*)k0, fa1 = *(const uint4*)k1;
 #pragma unroll
         for (int ks = 0; ks < PS::KS; ++ks) {
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + ks * 16));
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], sacc[mt], 0, 0, 0);
+          uint4 fb0, fb1;
+          if (ks + 1 < PS::KS) {
+            fb0 = *(const uint4*)(k0 + (ks + 1) * 16);
+            fb1 = *(const uint4*)(k1 + (ks + 1) * 16);
+          }
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa0), qreg[ks], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa1), qreg[ks], sacc[1], 0, 0, 0);
+          if (ks + 1 < PS::KS) {
+            fa0 = fb0;
+            fa1 = fb1;
+          }
         }
       }
       // Scores in the log2 domain are c * s (c = scale * log2 e).  The tile
@@ -373,14 +387,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
       l_run += psum;
-      // O^T += V^T P^T
+      // O^T += V^T P^T: the DT accumulators alternate; the V^T fragments
+      // of the next contraction step are read while this step's run
+      {
+        const uint16_t* v0 = vl + lq * PS::VROW + hh * 8;
+        uint4 fa[PS::DT], fb[PS::DT];
 #pragma unroll
-      for (int dt = 0; dt < PS::DT; ++dt) {
-        const uint16_t* vrow = vl + (dt * 32 + lq) * PS::VROW + hh * 8;
+        for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const uint4*)(vrow + kk * 16));
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], acc_o[dt], 0, 0, 0);
+          if (kk + 1 < 4) {
+#pragma unroll
+            for (int dt = 0; dt < PS::DT; ++dt) fb[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW + (kk + 1) * 16);
+          }
+#pragma unroll
+          for (int dt = 0; dt < PS::DT; ++dt)
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[dt]), pb[kk], acc_o[dt], 0, 0, 0);
+          if (kk + 1 < 4) {
+#pragma unroll
+            for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = fb[dt];
+          }
         }
       }
         }
