@@ -148,6 +148,47 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
     return res, (wl, st, out)
 
 
+def block_sweep(args, torch, np, api, driver, workloads, dev):
+    """Decode at the Llama-3.1-8B shape for several block sizes with the same
+    lengths and values (seed 2) and the same pool capacity (409,600 tokens
+    per layer): kernel time, KV GB/s and the share of allocated slots that
+    hold tokens (the tail waste of the last block)."""
+    rows = []
+    stream = torch.cuda.current_stream()
+    for B in args.block_sweep:
+        wl = workloads.llama_decode(2, 64, 128, 2048, 409_600 // B, f"llama31-8b-decode-b64-B{B}", block_size=B)
+        st = driver.run_script(wl, device=dev)
+        torch.cuda.synchronize()
+        S, Hq, Hkv, D = len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim
+        ctx = st.context_lens.astype(np.int64)
+        kv_bytes = int(ctx.sum()) * Hkv * D * 2 * 2
+        L = max(1, args.layers)
+        kps, vps = [st.k_pool], [st.v_pool]
+        for _ in range(1, L):
+            kps.append(st.k_pool.clone())
+            vps.append(st.v_pool.clone())
+        q = driver.to_device(wl.q, wl.dtype, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+                         dtype=torch.uint8, device=dev)
+
+        def decode(i):
+            api.paged_attention_decode(out, q, kps[i % L], vps[i % L], st.tables_dev, st.lens_dev,
+                                       float(wl.scale), workspace=ws)
+
+        ms, _ = timed_calls(torch, decode, args.steps, args.warmup, stream)
+        slots = int(((ctx + B - 1) // B * B).sum())
+        rows.append({"block_size": B, "decode_us_avg": round(ms * 1e3, 2),
+                     "kv_gbps": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+                     "useful_slot_ratio": round(int(ctx.sum()) / slots, 5),
+                     "waste_slots_per_seq": round((slots - int(ctx.sum())) / S, 2),
+                     "table_entries_per_seq": wl.max_blocks_per_seq})
+        log(f"block size {B}: {rows[-1]}")
+        del kps, vps, st
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +201,8 @@ def main():
     ap.add_argument("--no-copy-bandwidth", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
+                    help="instead of the benchmark, time decode at the Llama shape for these block sizes")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once with copy_blocks (a plain copy of known size, "
                          "for scaling HBM byte counters)")
@@ -176,6 +219,13 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.block_sweep is not None:
+        sizes = args.block_sweep or [8, 16, 32, 64, 128, 256]
+        args.block_sweep = sizes
+        rows = block_sweep(args, torch, np, api, driver, workloads, dev)
+        print(json.dumps({"block_sweep": rows, "workload": "llama31-8b-decode-b64 (seed 2), 409,600-token pool per "
+                          f"layer, {max(1, args.layers)} layers rotated", "steps": args.steps}), flush=True)
+        return
     t0 = time.time()
     wl = workloads.config2()
     log(f"workload {wl.name} generated in {time.time() - t0:.1f}s")

@@ -29,9 +29,10 @@
  *  - Device pointers to element arrays must be 16-byte aligned
  *    (PKV_ERR_ALIGN otherwise); int32 arrays need 4-byte alignment.
  *  - Supported shapes (PKV_ERR_UNSUPPORTED otherwise): dtype f32 or bf16;
- *    head_dim 16, 32, 64 or 128; block_size 1, 2, 4, 8, 16, 32 or 64;
+ *    head_dim 16, 32, 64 or 128; block_size a power of two from 1 to 256;
  *    num_heads / num_kv_heads in {1, 2, 4, 8} with head_dim * elem_bytes
- *    / 16 >= that ratio.  Prefill: bf16, head_dim 64 or 128, block_size 8..64.
+ *    / 16 >= that ratio.  Prefill: bf16, head_dim 64 or 128, any of those
+ *    block sizes.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

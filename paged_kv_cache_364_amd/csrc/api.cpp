@@ -51,7 +51,7 @@ bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int elem_bytes(int dtype) { return dtype == PKV_DTYPE_F32 ? 4 : dtype == PKV_DTYPE_BF16 ? 2 : 0; }
 
 bool head_dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
-bool block_ok(int B) { return pow2(B) && B <= 64; }
+bool block_ok(int B) { return pow2(B) && B <= 256; }
 
 // Common checks of the cache geometry.
 int check_cache(int num_blocks, int Hkv, int B, int D, int dtype) {

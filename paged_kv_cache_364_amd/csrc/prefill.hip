@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 
 bool prefill_supported(int dtype, int head_dim, int group, int block_size) {
   (void)group;
-  return dtype == 1 && (head_dim == 64 || head_dim == 128) && block_size >= 1 && block_size <= 64 &&
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && block_size >= 1 && block_size <= 256 &&
          (block_size & (block_size - 1)) == 0;
 }
 

@@ -227,13 +227,14 @@ def config1():
                            scale=np.float32(0.25))
 
 
-def llama_decode(seed=2, num_seqs=64, lo=128, hi=2048, num_blocks=25_600, name=None):
-    """Llama-3.1-8B-shaped decode, batch ``num_seqs``, context ~ U{lo..hi}."""
+def llama_decode(seed=2, num_seqs=64, lo=128, hi=2048, num_blocks=25_600, name=None, block_size=16):
+    """Llama-3.1-8B-shaped decode, batch ``num_seqs``, context ~ U{lo..hi}.
+    The same seed gives the same lengths and values for any block size."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi + 1, size=num_seqs)
     wl = decode_workload(name or f"llama31-8b-decode-b{num_seqs}", rng.integers(1 << 62), lens,
-                         **LLAMA, block_size=16, num_blocks=num_blocks, dtype=BF16,
-                         max_blocks_per_seq=-(-hi // 16))
+                         **LLAMA, block_size=block_size, num_blocks=num_blocks, dtype=BF16,
+                         max_blocks_per_seq=-(-hi // block_size))
     return wl
 
 

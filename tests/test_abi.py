@@ -75,7 +75,8 @@ def test_decode_rejects_bad_arguments():
     assert call(Hq=6) == N.PKV_ERR_UNSUPPORTED      # group 3
     assert call(Hq=32) == N.PKV_ERR_UNSUPPORTED     # group 16
     assert call(D=48) == N.PKV_ERR_UNSUPPORTED
-    assert call(B=128) == N.PKV_ERR_UNSUPPORTED
+    assert call(B=512) == N.PKV_ERR_UNSUPPORTED
+    assert call(B=48) == N.PKV_ERR_UNSUPPORTED
     assert call(Hkv=0) == N.PKV_ERR_INVALID
     assert call(S=-1) == N.PKV_ERR_INVALID
     assert call(mb=0) == N.PKV_ERR_INVALID

@@ -75,7 +75,7 @@ VARIANTS = [
     ("f32", 128, 1, 16), ("f32", 128, 4, 16), ("f32", 128, 8, 2),
     ("bf16", 16, 1, 16), ("bf16", 16, 2, 4), ("bf16", 32, 4, 32), ("bf16", 64, 8, 16), ("bf16", 64, 1, 8),
     ("bf16", 128, 1, 16), ("bf16", 128, 2, 64), ("bf16", 128, 4, 16), ("bf16", 128, 4, 4), ("bf16", 128, 4, 32),
-    ("bf16", 128, 8, 16), ("bf16", 128, 4, 1),
+    ("bf16", 128, 8, 16), ("bf16", 128, 4, 1), ("bf16", 128, 4, 128), ("bf16", 128, 4, 256), ("f32", 64, 2, 256),
 ]
 
 

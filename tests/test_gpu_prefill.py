@@ -63,7 +63,7 @@ def test_prefill_small_mha():
 
 @pytest.mark.parametrize("hq,hkv,d,b", [
     (8, 2, 128, 16), (8, 2, 64, 16), (4, 4, 64, 8), (6, 3, 128, 32), (4, 1, 128, 64), (2, 2, 64, 1),
-    (8, 8, 128, 4),
+    (8, 8, 128, 4), (8, 2, 128, 128), (4, 4, 64, 256),
 ])
 def test_prefill_variants(hq, hkv, d, b):
     check(small(f"pf-{hq}-{hkv}-{d}-{b}", 60 + hq + d + b, [0, 5, 100, 63], [17, 64, 77, 129], hq, hkv, d, b))
