@@ -148,6 +148,39 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
     return res, (wl, st, out)
 
 
+def swap_leg(torch, api, dev, n_blocks=4096):
+    """Swap-out and swap-in of n whole Llama-shape blocks (64 KiB of K + V
+    each) between a pool and pinned host memory, against a plain DMA copy of
+    the same bytes to and from pinned memory."""
+    Hkv, B, D = 8, 16, 128
+    k = torch.empty((4 * n_blocks, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    k.view(torch.int16).fill_(5)
+    v.view(torch.int16).fill_(6)
+    ids = torch.randperm(4 * n_blocks, device=dev)[:n_blocks].to(torch.int32).contiguous()
+    hk = torch.empty((n_blocks, Hkv, B, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    nbytes = 2 * hk.numel() * 2
+    out_ms, _ = timed_calls(torch, lambda i: api.swap_out(k, v, ids, hk, hv), 5, 2, stream)
+    in_ms, _ = timed_calls(torch, lambda i: api.swap_in(k, v, ids, hk, hv), 5, 2, stream)
+    dk = torch.empty((n_blocks, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    d2h_ms, _ = timed_calls(torch, lambda i: (hk.copy_(dk, non_blocking=True), hv.copy_(dk, non_blocking=True)),
+                            5, 2, stream)
+    h2d_ms, _ = timed_calls(torch, lambda i: (dk.copy_(hk, non_blocking=True), dk.copy_(hv, non_blocking=True)),
+                            5, 2, stream)
+    torch.cuda.synchronize()
+    res = {"blocks": n_blocks, "bytes": nbytes,
+           "swap_out_gbps": round(nbytes / (out_ms * 1e-3) / 1e9, 2),
+           "swap_in_gbps": round(nbytes / (in_ms * 1e-3) / 1e9, 2),
+           "dma_d2h_gbps": round(nbytes / (d2h_ms * 1e-3) / 1e9, 2),
+           "dma_h2d_gbps": round(nbytes / (h2d_ms * 1e-3) / 1e9, 2)}
+    log(f"swap: {res}")
+    del k, v, dk
+    torch.cuda.empty_cache()
+    return res
+
+
 def block_sweep(args, torch, np, api, driver, workloads, dev):
     """Decode at the Llama-3.1-8B shape for several block sizes with the same
     lengths and values (seed 2) and the same pool capacity (409,600 tokens
@@ -199,6 +232,7 @@ def main():
     ap.add_argument("--prefill-layers", type=int, default=40)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-copy-bandwidth", action="store_true")
+    ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
@@ -349,6 +383,9 @@ def main():
         result["copy_kernel_gbps"] = round(cbw, 1)
         result["roofline"]["frac_of_copy_kernel"] = round(achieved / cbw, 4)
         log(f"copy_blocks bandwidth (read + write) {cbw:.0f} GB/s")
+
+    if not args.no_swap:
+        result["swap"] = swap_leg(torch, api, dev)
 
     pf = None
     if not args.no_prefill:

@@ -96,6 +96,30 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_
                     int num_kv_heads, int block_size, int head_dim, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * swap_out / swap_in: move whole blocks between the device pools and host
+ * memory, for preemption by swapping (intelliparadigm.com article, sections
+ * 3.1 and 6.1: blocks of a preempted request go to CPU memory and come back
+ * later; "08. PagedAttention", section "what it does not solve").
+ *
+ *   block_ids        device int32 [num]: physical blocks, in the order of the
+ *                    host buffers
+ *   host_k, host_v   host memory [num][num_kv_heads][block_size][head_dim]
+ *                    of dtype, pinned (hipHostMalloc or torch pin_memory) so
+ *                    the GPU reads / writes it directly; 16-byte aligned;
+ *                    caller-owned and not to be touched until the call has
+ *                    completed on `stream`
+ * swap_out: host[i] = cache[block_ids[i]]; swap_in: cache[block_ids[i]] =
+ * host[i]; K and V, every head and slot, bitwise.  Ids outside
+ * [0, num_blocks) are skipped; swap_in's ids must be distinct.
+ * ---------------------------------------------------------------------- */
+int pkv_swap_out(const void* k_cache, const void* v_cache, const int32_t* block_ids, int num, int num_blocks,
+                 int num_kv_heads, int block_size, int head_dim, int dtype, void* host_k, void* host_v,
+                 void* stream);
+
+int pkv_swap_in(void* k_cache, void* v_cache, const int32_t* block_ids, int num, int num_blocks, int num_kv_heads,
+                int block_size, int head_dim, int dtype, const void* host_k, const void* host_v, void* stream);
+
+/* ------------------------------------------------------------------------
  * paged_attention_decode: one query token per sequence.
  * out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over the first
  * context_lens[s] tokens of sequence s, K_s / V_s read through the block
@@ -197,6 +221,19 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos);
 /* Release a sequence.  PKV_ERR_INVALID if unknown; PKV_ERR_STATE on a
  * reference-count underflow (never happens through this API). */
 int pkv_seq_free(pkv_alloc* a, int64_t seq);
+
+/* Swap a sequence out: blocks_out (host int32 [cap]) receives its table in
+ * logical order -- the blocks to copy to host memory with pkv_swap_out
+ * before they are reused -- and *num_out its length; the blocks are then
+ * released exactly as pkv_seq_free would, and the sequence keeps its length
+ * but holds no blocks.  Append, fork and pkv_build_block_tables on a swapped
+ * sequence give PKV_ERR_STATE; pkv_seq_free drops it.
+ * Swap it back in: takes *num_out fresh blocks off the free list (logical
+ * order; PKV_ERR_NO_BLOCKS and no change if too few are free) and writes
+ * them to blocks_out: host buffer i goes to block blocks_out[i]
+ * (pkv_swap_in).  PKV_ERR_STATE if the sequence is not swapped out. */
+int pkv_seq_swap_out(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int* num_out);
+int pkv_seq_swap_in(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int* num_out);
 
 int pkv_seq_len(const pkv_alloc* a, int64_t seq, int64_t* len_out);
 

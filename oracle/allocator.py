@@ -35,6 +35,17 @@ another):
   the parent (ref + 1 each) and length f.
 * ``append`` is atomic: it first counts the blocks it needs and fails with
   no change when the free list is too short.
+
+Swapping (preemption by swap: the intelliparadigm.com article, sections 3.1
+and 6.1, moves a preempted request's blocks to CPU memory and back; "08.
+PagedAttention", section "what it does not solve"):
+
+* ``swap_out`` returns the sequence's table (the blocks whose contents must
+  reach host memory) and then gives the blocks back exactly as ``release``
+  does; the sequence keeps its length and holds no blocks.
+* ``swap_in`` takes as many fresh blocks off the free list as it had, in
+  logical order (all or nothing); host buffer i goes to the i-th of them.
+* append, fork and table export refuse a swapped sequence; release drops it.
 """
 from __future__ import annotations
 
@@ -63,6 +74,7 @@ class BlockAllocator:
         self.ref: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.swapped: Dict[int, int] = {}  # seq -> table length when swapped out
 
     # -- sequence lifecycle -------------------------------------------------
     def add(self, seq: int) -> None:
@@ -80,6 +92,8 @@ class BlockAllocator:
         the tokens are written."""
         if seq not in self.tables:
             raise AllocatorError(f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise AllocatorError(f"sequence {seq} is swapped out")
         if n < 0:
             raise AllocatorError("negative token count")
         B = self.block_size
@@ -124,6 +138,8 @@ class BlockAllocator:
             raise AllocatorError(f"unknown sequence {parent}")
         if child in self.tables:
             raise AllocatorError(f"sequence {child} exists")
+        if parent in self.swapped:
+            raise AllocatorError(f"sequence {parent} is swapped out")
         if not 0 <= fork_pos <= self.lens[parent]:
             raise AllocatorError("fork position outside the parent")
         nb = -(-fork_pos // self.block_size)
@@ -133,17 +149,46 @@ class BlockAllocator:
         self.tables[child] = list(shared)
         self.lens[child] = fork_pos
 
-    def release(self, seq: int) -> None:
-        if seq not in self.tables:
-            raise AllocatorError(f"unknown sequence {seq}")
-        for b in reversed(self.tables[seq]):
+    def _give_back(self, table: List[int]) -> None:
+        for b in reversed(table):
             if self.ref[b] <= 0:
                 raise AllocatorError("reference count underflow")
+        for b in reversed(table):
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
+
+    def release(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        self._give_back(self.tables[seq])
         del self.tables[seq]
         del self.lens[seq]
+        self.swapped.pop(seq, None)
+
+    def swap_out(self, seq: int) -> List[int]:
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise AllocatorError(f"sequence {seq} is already swapped out")
+        table = list(self.tables[seq])
+        self._give_back(table)
+        self.tables[seq] = []
+        self.swapped[seq] = len(table)
+        return table
+
+    def swap_in(self, seq: int) -> List[int]:
+        if seq not in self.swapped:
+            raise AllocatorError(f"sequence {seq} is not swapped out")
+        n = self.swapped[seq]
+        if n > len(self.free):
+            raise OutOfBlocks(f"need {n} blocks, {len(self.free)} free")
+        table = [self._pop() for _ in range(n)]
+        for b in table:
+            self.ref[b] = 1
+        self.tables[seq] = table
+        del self.swapped[seq]
+        return list(table)
 
     # -- queries ------------------------------------------------------------
     def table(self, seq: int) -> List[int]:
@@ -165,6 +210,8 @@ class BlockAllocator:
         t = np.full((len(seqs), max(width, 1)), -1, dtype=np.int32)
         lens = np.zeros(len(seqs), dtype=np.int32)
         for i, s in enumerate(seqs):
+            if s in self.swapped:
+                raise AllocatorError(f"sequence {s} is swapped out")
             row = self.tables[s]
             if len(row) > width:
                 raise AllocatorError("table wider than the padded width")

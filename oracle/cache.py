@@ -17,6 +17,9 @@ NaN poison survives unchanged.
   (intelliparadigm.com article, section 2.3: allocate a new block, copy the
   original block's contents).  All sources are read before any destination
   is written.
+* ``swap_out`` / ``swap_in``: whole blocks to and from a host buffer whose
+  entry i is block ids[i] (intelliparadigm.com article, sections 3.1 and
+  6.1: a preempted request's blocks go to CPU memory and come back).
 """
 from __future__ import annotations
 
@@ -61,3 +64,17 @@ def copy_blocks(pool: np.ndarray, pairs) -> None:
     dst = np.array([b for _, b in pairs])
     data = pool[src].copy()  # read every source first
     pool[dst] = data
+
+
+def swap_out(pool: np.ndarray, ids) -> np.ndarray:
+    """Host buffer [n, H_kv, B, D]: entry i is block ids[i] of the pool."""
+    out = np.empty((len(ids),) + pool.shape[1:], dtype=pool.dtype)
+    for i, b in enumerate(ids):
+        out[i] = pool[int(b)]
+    return out
+
+
+def swap_in(pool: np.ndarray, ids, host: np.ndarray) -> None:
+    """Block ids[i] of the pool becomes host entry i."""
+    for i, b in enumerate(ids):
+        pool[int(b)] = host[i]

@@ -11,6 +11,8 @@ from .api import (  # noqa: F401
     kv_write,
     paged_attention_decode,
     paged_attention_prefill,
+    swap_in,
+    swap_out,
 )
 from .allocator import BlockAllocator, OutOfBlocks  # noqa: F401
 from ._native import PagedKVError  # noqa: F401

@@ -53,6 +53,8 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [c_int]),
     "pkv_kv_write": (c_int, [vp, vp, vp, c_int, vp, vp, c_int, c_int, c_int, c_int, c_int, vp]),
     "pkv_copy_blocks": (c_int, [vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]),
+    "pkv_swap_out": (c_int, [vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp]),
+    "pkv_swap_in": (c_int, [vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp]),
     "pkv_decode_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "pkv_paged_attention_decode": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_float, c_int, vp, c_size, vp]),
@@ -64,6 +66,8 @@ SIGNATURES = {
     "pkv_seq_append": (c_int, [vp, c_i64, c_int, i32p, i32p, c_int, intp]),
     "pkv_seq_fork": (c_int, [vp, c_i64, c_i64, c_int]),
     "pkv_seq_free": (c_int, [vp, c_i64]),
+    "pkv_seq_swap_out": (c_int, [vp, c_i64, i32p, c_int, intp]),
+    "pkv_seq_swap_in": (c_int, [vp, c_i64, i32p, c_int, intp]),
     "pkv_seq_len": (c_int, [vp, c_i64, i64p]),
     "pkv_get_block_table": (c_int, [vp, c_i64, i32p, c_int, intp]),
     "pkv_build_block_tables": (c_int, [vp, i64p, c_int, c_int, i32p, i32p]),

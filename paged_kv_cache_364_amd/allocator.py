@@ -62,6 +62,25 @@ class BlockAllocator:
     def release(self, seq: int) -> None:
         N.check(self._L.pkv_seq_free(self._h, int(seq)), "seq_free")
 
+    def _blocks_call(self, fn, seq: int, what: str) -> List[int]:
+        n = ctypes.c_int(0)
+        out = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        st = fn(self._h, int(seq), out.ctypes.data_as(N.i32p), self.num_blocks, ctypes.byref(n))
+        if st == N.PKV_ERR_NO_BLOCKS:
+            raise OutOfBlocks(st, what)
+        N.check(st, what)
+        return out[: n.value].tolist()
+
+    def swap_out(self, seq: int) -> List[int]:
+        """Release the sequence's blocks (pkv_seq_swap_out); returns its
+        table, the blocks whose contents go to host memory."""
+        return self._blocks_call(self._L.pkv_seq_swap_out, seq, "seq_swap_out")
+
+    def swap_in(self, seq: int) -> List[int]:
+        """Fresh blocks for a swapped-out sequence (pkv_seq_swap_in); host
+        buffer i goes to returned block i."""
+        return self._blocks_call(self._L.pkv_seq_swap_in, seq, "seq_swap_in")
+
     def length(self, seq: int) -> int:
         x = ctypes.c_int64(0)
         N.check(self._L.pkv_seq_len(self._h, int(seq), ctypes.byref(x)), "seq_len")

@@ -72,6 +72,37 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tenso
         N_, H, B, D, _dtype_code(k_cache), _stream(stream)), "copy_blocks")
 
 
+def _pinned(t: torch.Tensor, name: str, shape, dtype) -> int:
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (torch.empty(..., pin_memory=True))")
+    if not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+def swap_out(k_cache: torch.Tensor, v_cache: torch.Tensor, block_ids: torch.Tensor, host_k: torch.Tensor,
+             host_v: torch.Tensor, stream=None) -> None:
+    """host_k/host_v[i] = k_cache/v_cache[block_ids[i]] (pkv_swap_out); host
+    tensors pinned, [n, num_kv_heads, block_size, head_dim]."""
+    N_, H, B, D = _cache_geometry(k_cache, v_cache)
+    n = block_ids.numel()
+    N.check(N.lib().pkv_swap_out(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_ids, "block_ids", torch.int32), n, N_, H, B,
+        D, _dtype_code(k_cache), _pinned(host_k, "host_k", (n, H, B, D), k_cache.dtype),
+        _pinned(host_v, "host_v", (n, H, B, D), k_cache.dtype), _stream(stream)), "swap_out")
+
+
+def swap_in(k_cache: torch.Tensor, v_cache: torch.Tensor, block_ids: torch.Tensor, host_k: torch.Tensor,
+            host_v: torch.Tensor, stream=None) -> None:
+    """k_cache/v_cache[block_ids[i]] = host_k/host_v[i] (pkv_swap_in)."""
+    N_, H, B, D = _cache_geometry(k_cache, v_cache)
+    n = block_ids.numel()
+    N.check(N.lib().pkv_swap_in(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_ids, "block_ids", torch.int32), n, N_, H, B,
+        D, _dtype_code(k_cache), _pinned(host_k, "host_k", (n, H, B, D), k_cache.dtype),
+        _pinned(host_v, "host_v", (n, H, B, D), k_cache.dtype), _stream(stream)), "swap_in")
+
+
 def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                           max_blocks_per_seq: int, dtype: torch.dtype) -> int:
     n = N.lib().pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

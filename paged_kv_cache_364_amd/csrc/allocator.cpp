@@ -16,6 +16,12 @@
 // free stack seeded with init_order[0] on top; release pushes a sequence's
 // blocks last-to-first; copy only when ref > 1 at the first write into the
 // block (the last holder writes in place); appends are all-or-nothing.
+//
+// Swapping (preemption by swap, intelliparadigm.com article, sections 3.1
+// and 6.1; "08. PagedAttention", section "what it does not solve"): a
+// swapped-out sequence gives its blocks back exactly as a release would,
+// keeps its length, and holds no blocks until it is swapped in, which takes
+// fresh blocks off the free list in logical order (all-or-nothing).
 #include <stdint.h>
 
 #include <new>
@@ -28,6 +34,8 @@ struct pkv_alloc {
   struct Seq {
     std::vector<int32_t> table;
     int64_t len = 0;
+    bool swapped = false;
+    int64_t swapped_blocks = 0;  // table length when it was swapped out
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
@@ -83,6 +91,7 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PKV_ERR_INVALID;
   pkv_alloc::Seq& s = it->second;
+  if (s.swapped) return PKV_ERR_STATE;
   const int64_t B = a->block_size;
   const int64_t start = s.len;
   const int64_t end = start + n;
@@ -133,6 +142,7 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos) {
   if (!a) return PKV_ERR_INVALID;
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end() || a->seqs.count(child)) return PKV_ERR_INVALID;
+  if (it->second.swapped) return PKV_ERR_STATE;
   if (fork_pos < 0 || fork_pos > it->second.len) return PKV_ERR_INVALID;
   const int64_t nb = ((int64_t)fork_pos + a->block_size - 1) / a->block_size;
   pkv_alloc::Seq c;
@@ -158,6 +168,54 @@ int pkv_seq_free(pkv_alloc* a, int64_t seq) {
     if (--a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
   }
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_seq_swap_out(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int* num_out) {
+  if (!a || !num_out) return PKV_ERR_INVALID;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_ERR_INVALID;
+  pkv_alloc::Seq& s = it->second;
+  if (s.swapped) return PKV_ERR_STATE;
+  const std::vector<int32_t>& t = s.table;
+  *num_out = (int)t.size();
+  if ((int64_t)t.size() > cap || (!t.empty() && !blocks_out)) return PKV_ERR_INVALID;
+  for (auto b = t.rbegin(); b != t.rend(); ++b)
+    if (a->ref[(size_t)*b] <= 0) return PKV_ERR_STATE;
+  for (size_t i = 0; i < t.size(); ++i) blocks_out[i] = t[i];
+  for (auto b = t.rbegin(); b != t.rend(); ++b) {
+    if (--a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
+  }
+  s.swapped_blocks = (int64_t)t.size();
+  s.table.clear();
+  s.swapped = true;
+  return PKV_OK;
+}
+
+int pkv_seq_swap_in(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int* num_out) {
+  if (!a || !num_out) return PKV_ERR_INVALID;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_ERR_INVALID;
+  pkv_alloc::Seq& s = it->second;
+  if (!s.swapped) return PKV_ERR_STATE;
+  const int64_t n = s.swapped_blocks;
+  *num_out = (int)n;
+  if (n > cap || (n > 0 && !blocks_out)) return PKV_ERR_INVALID;
+  if (n > (int64_t)a->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+  try {
+    s.table.reserve((size_t)n);
+  } catch (...) {
+    return PKV_ERR_STATE;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t b = a->free_stack.back();
+    a->free_stack.pop_back();
+    a->ref[(size_t)b] = 1;
+    s.table.push_back(b);
+    blocks_out[i] = b;
+  }
+  s.swapped = false;
+  s.swapped_blocks = 0;
   return PKV_OK;
 }
 
@@ -187,6 +245,7 @@ int pkv_build_block_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs
   for (int i = 0; i < num_seqs; ++i) {
     auto it = a->seqs.find(seqs[i]);
     if (it == a->seqs.end()) return PKV_ERR_INVALID;
+    if (it->second.swapped) return PKV_ERR_STATE;
     if ((int64_t)it->second.table.size() > max_blocks_per_seq || it->second.len > INT32_MAX)
       return PKV_ERR_INVALID;
   }

@@ -108,6 +108,34 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_
                                  elem_bytes(dtype), (hipStream_t)stream);
 }
 
+static int swap_blocks(bool out, void* k_cache, void* v_cache, const int32_t* block_ids, int num, int num_blocks,
+                       int num_kv_heads, int block_size, int head_dim, int dtype, void* host_k, void* host_v,
+                       void* stream) {
+  int st = check_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype);
+  if (st) return st;
+  if (num < 0) return PKV_ERR_INVALID;
+  if (num == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_ids || !host_k || !host_v) return PKV_ERR_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(host_k) || !aligned16(host_v) ||
+      !aligned4(block_ids))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_swap_blocks(out, k_cache, v_cache, block_ids, num, num_blocks, num_kv_heads, block_size,
+                                 head_dim, elem_bytes(dtype), host_k, host_v, (hipStream_t)stream);
+}
+
+int pkv_swap_out(const void* k_cache, const void* v_cache, const int32_t* block_ids, int num, int num_blocks,
+                 int num_kv_heads, int block_size, int head_dim, int dtype, void* host_k, void* host_v,
+                 void* stream) {
+  return swap_blocks(true, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_ids, num, num_blocks,
+                     num_kv_heads, block_size, head_dim, dtype, host_k, host_v, stream);
+}
+
+int pkv_swap_in(void* k_cache, void* v_cache, const int32_t* block_ids, int num, int num_blocks, int num_kv_heads,
+                int block_size, int head_dim, int dtype, const void* host_k, const void* host_v, void* stream) {
+  return swap_blocks(false, k_cache, v_cache, block_ids, num, num_blocks, num_kv_heads, block_size, head_dim, dtype,
+                     const_cast<void*>(host_k), const_cast<void*>(host_v), stream);
+}
+
 static int check_attention(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                            int num_blocks, int max_blocks, int dtype) {
   int st = check_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype);

@@ -94,4 +94,53 @@ int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+// Swap of whole blocks between the device pools and caller-provided host
+// memory (pinned, so the GPU reads and writes it directly over the bus):
+// out: host[i] = cache[ids[i]]; in: cache[ids[i]] = host[i], for K and V.
+// grid.y walks the blocks, grid.x lanes stride over a block's bytes.
+template <bool OUT>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                          const int32_t* __restrict__ ids, int n, int num_blocks,
+                                                          size_t block_bytes, char* __restrict__ hk,
+                                                          char* __restrict__ hv) {
+  for (int i = blockIdx.y; i < n; i += gridDim.y) {
+    const int b = ids[i];
+    if ((unsigned)b >= (unsigned)num_blocks) continue;
+    char* dk = kc + (size_t)b * block_bytes;
+    char* dv = vc + (size_t)b * block_bytes;
+    char* pk = hk + (size_t)i * block_bytes;
+    char* pv = hv + (size_t)i * block_bytes;
+    for (size_t off = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes;
+         off += (size_t)gridDim.x * blockDim.x * 16) {
+      if (OUT) {
+        const uint4 x = *(const uint4*)(dk + off);
+        const uint4 y = *(const uint4*)(dv + off);
+        *(uint4*)(pk + off) = x;
+        *(uint4*)(pv + off) = y;
+      } else {
+        const uint4 x = *(const uint4*)(pk + off);
+        const uint4 y = *(const uint4*)(pv + off);
+        *(uint4*)(dk + off) = x;
+        *(uint4*)(dv + off) = y;
+      }
+    }
+  }
+}
+
+int launch_swap_blocks(bool out, void* k_cache, void* v_cache, const int32_t* ids, int n, int num_blocks, int Hkv,
+                       int B, int D, int elem_bytes, void* host_k, void* host_v, hipStream_t stream) {
+  if (n == 0) return 0;
+  const size_t block_bytes = (size_t)Hkv * B * D * elem_bytes;
+  unsigned gx = (unsigned)std::min<size_t>((block_bytes / 16 + 255) / 256, 64);
+  if (gx == 0) gx = 1;
+  const unsigned gy = (unsigned)std::min(n, 65535);
+  if (out)
+    hipLaunchKernelGGL(swap_blocks_kernel<true>, dim3(gx, gy), dim3(256), 0, stream, (char*)k_cache,
+                       (char*)v_cache, ids, n, num_blocks, block_bytes, (char*)host_k, (char*)host_v);
+  else
+    hipLaunchKernelGGL(swap_blocks_kernel<false>, dim3(gx, gy), dim3(256), 0, stream, (char*)k_cache,
+                       (char*)v_cache, ids, n, num_blocks, block_bytes, (char*)host_k, (char*)host_v);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 }  // namespace pkv

@@ -77,15 +77,15 @@ def test_random_ops_match():
         order = rng.permutation(N)
         a = BlockAllocator(N, B, order)
         o = OracleAlloc(N, B, order)
-        live, nxt = [], 0
+        live, swapped, nxt = [], [], 0
         for _ in range(300):
             r = rng.random()
-            if r < 0.25 or not live:
+            if r < 0.2 or not live:
                 a.add(nxt)
                 o.add(nxt)
                 live.append(nxt)
                 nxt += 1
-            elif r < 0.65:
+            elif r < 0.55:
                 s = live[rng.integers(len(live))]
                 n = int(rng.integers(0, 3 * B))
                 try:
@@ -96,18 +96,56 @@ def test_random_ops_match():
                 else:
                     s1, c1 = a.append(s, n)
                     assert s1.tolist() == s2 and c1 == c2
-            elif r < 0.8:
+            elif r < 0.68:
                 s = live[rng.integers(len(live))]
                 f = int(rng.integers(0, o.length(s) + 1))
                 a.fork(s, nxt, f)
                 o.fork(s, nxt, f)
                 live.append(nxt)
                 nxt += 1
-            else:
+            elif r < 0.78:
                 s = live.pop(rng.integers(len(live)))
+                assert a.swap_out(s) == o.swap_out(s)
+                swapped.append(s)
+            elif r < 0.88 and swapped:
+                s = swapped[rng.integers(len(swapped))]
+                try:
+                    t2 = o.swap_in(s)
+                except OracleOOB:
+                    with pytest.raises(OutOfBlocks):
+                        a.swap_in(s)
+                else:
+                    assert a.swap_in(s) == t2
+                    swapped.remove(s)
+                    live.append(s)
+            else:
+                pool = live + swapped
+                s = pool[rng.integers(len(pool))]
                 a.release(s)
                 o.release(s)
+                (live if s in live else swapped).remove(s)
             same_state(a, o)
+
+
+def test_swapped_sequence_refuses_append_and_fork():
+    a = BlockAllocator(8, 4)
+    a.add(0)
+    a.append(0, 6)
+    assert a.swap_out(0) == [0, 1]
+    assert a.table(0) == [] and a.length(0) == 6 and a.num_free() == 8
+    for bad in (lambda: a.append(0, 1), lambda: a.fork(0, 1, 2), lambda: a.block_tables([0], 4),
+                lambda: a.swap_out(0)):
+        with pytest.raises(PagedKVError) as e:
+            bad()
+        assert e.value.status == _native.PKV_ERR_STATE
+    a.add(5)
+    a.append(5, 32)  # takes all 8 blocks
+    with pytest.raises(OutOfBlocks):
+        a.swap_in(0)
+    assert a.table(0) == [] and a.num_free() == 0
+    a.release(5)
+    assert a.swap_in(0) == [0, 1]  # LIFO: block 0 was released last-to-first, so it is on top
+    assert a.append(0, 3)[0].tolist() == [6, 7, 8]
 
 
 def test_worked_example_b4():

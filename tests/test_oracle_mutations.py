@@ -178,3 +178,24 @@ def test_brute_force_transposed_is_caught(monkeypatch):
     brute_force.__wrapped__ = real
     monkeypatch.setattr(attention, "brute_force", brute_force)
     assert fails(P.check_hand_golden)
+
+
+def test_swap_in_order_mistake_is_caught(monkeypatch):
+    real = oracle.cache.swap_in
+
+    def reversed_swap_in(pool, ids, host):
+        real(pool, list(ids)[::-1], host)
+
+    monkeypatch.setattr(oracle.cache, "swap_in", reversed_swap_in)
+    assert fails(P.check_swap_roundtrip)
+
+
+def test_swap_out_keeping_blocks_is_caught(monkeypatch):
+    def swap_out_without_release(self, seq):
+        table = list(self.tables[seq])
+        self.tables[seq] = []
+        self.swapped[seq] = len(table)
+        return table
+
+    monkeypatch.setattr(BlockAllocator, "swap_out", swap_out_without_release)
+    assert fails(P.check_swap_allocator)

@@ -515,3 +515,70 @@ def test_ragged_lengths_and_churn():
     # fragmentation: some real sequence's blocks are not one contiguous run
     runs = [np.diff(row[row >= 0]) for row in st.tables]
     assert any((r != 1).any() for r in runs if r.size)
+
+
+# ---------------------------------------------------------------------------
+# swapping (intelliparadigm.com article, sections 3.1 and 6.1)
+# ---------------------------------------------------------------------------
+def check_swap_allocator():
+    """A swapped-out sequence gives its blocks back exactly as a release
+    does, keeps its length, and comes back on fresh blocks taken off the
+    free list in logical order."""
+    order = [8, 3, 15, 21] + [b for b in range(32) if b not in (8, 3, 15, 21)]
+    a = oracle.allocator.BlockAllocator(32, 4, order)
+    twin = oracle.allocator.BlockAllocator(32, 4, order)
+    for x in (a, twin):
+        x.add(0)
+        x.append(0, 10)
+    assert a.swap_out(0) == [8, 3, 15]
+    twin.release(0)
+    assert a.free == twin.free and a.ref == twin.ref
+    assert a.length(0) == 10 and a.table(0) == []
+    a.add(1)
+    a.append(1, 5)  # takes 8 and 3 again
+    assert a.table(1) == [8, 3]
+    assert a.swap_in(0) == [15, 21, order[4]]
+    assert a.table(0) == [15, 21, order[4]]
+    slots, _ = a.append(0, 1)  # position 10 -> logical block 2, offset 2
+    assert slots == [order[4] * 4 + 2]
+    allocator_invariants(a)
+
+
+def test_swap_allocator():
+    check_swap_allocator()
+
+
+def check_swap_roundtrip():
+    """Swap three sequences out to a host buffer, let other sequences reuse
+    and overwrite their blocks, swap them back in: every token's K and V is
+    where the new table says, and attention is bitwise unchanged."""
+    wl = W.decode_workload("swap-rt", 31, [9, 17, 4, 30, 12], num_heads=4, num_kv_heads=2, head_dim=8,
+                           block_size=4, num_blocks=40, dtype="f32")
+    st = runner.run(wl)
+    before = runner.expected(wl, st)
+    a = st.alloc
+    out_ids = {s: a.swap_out(s) for s in (1, 3, 4)}
+    host = {s: (oracle.cache.swap_out(st.k_pool, ids), oracle.cache.swap_out(st.v_pool, ids))
+            for s, ids in out_ids.items()}
+    for s, ids in out_ids.items():
+        assert np.array_equal(host[s][0], st.k_pool[ids])
+    # a filler takes (and overwrites) the freed blocks
+    a.add(99)
+    fill, _ = a.append(99, 4 * len(a.free))
+    junk = np.full((len(fill), 2, 8), 7.0, dtype=np.float32).view(np.uint32)
+    oracle.cache.kv_write(st.k_pool, junk, fill)
+    oracle.cache.kv_write(st.v_pool, junk, fill)
+    a.release(99)
+    for s in (4, 1, 3):
+        ids = a.swap_in(s)
+        assert len(ids) == len(out_ids[s])
+        oracle.cache.swap_in(st.k_pool, ids, host[s][0])
+        oracle.cache.swap_in(st.v_pool, ids, host[s][1])
+    tables, lens = a.block_tables(wl.batch, wl.max_blocks_per_seq)
+    after = oracle.attention.decode(wl.q, st.k_pool, st.v_pool, tables, lens, wl.scale, wl.dtype)
+    assert np.array_equal(before, after)
+    assert not np.array_equal(tables, st.tables)  # the blocks did move
+
+
+def test_swap_roundtrip():
+    check_swap_roundtrip()
