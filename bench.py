@@ -181,6 +181,37 @@ def swap_leg(torch, api, dev, n_blocks=4096):
     return res
 
 
+def prefix_cache_leg(torch, np, api, driver, workloads, dev, steps, warmup):
+    """32 requests sharing a 1,024-token system prompt (plus U{1..256}
+    own tokens each), allocated with and without the prefix cache: blocks
+    held, K/V rows written, and the decode time over each batch."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    for use in (True, False):
+        wl = workloads.shared_prompt_requests(6, 32, 1024, 256, 25_600, use_cache=use)
+        st = driver.run_script(wl, device=dev)
+        q = driver.to_device(wl.q, wl.dtype, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                                                   wl.block_size, wl.max_blocks_per_seq, q.dtype),
+                         dtype=torch.uint8, device=dev)
+
+        def decode(i):
+            api.paged_attention_decode(out, q, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev, float(wl.scale),
+                                       workspace=ws)
+
+        ms, _ = timed_calls(torch, decode, steps, warmup, stream)
+        key = "with_cache" if use else "without_cache"
+        res[key] = {"blocks_held": int(st.alloc.stats().num_used),
+                    "kv_rows_written": int(sum(1 for x in st.step_slots[0] if x >= 0)),
+                    "decode_us_avg": round(ms * 1e3, 2)}
+        del st
+        torch.cuda.empty_cache()
+    res["workload"] = "32 requests x (1,024-token shared prompt + U{1..256}), Llama-3.1-8B shape, B=16 (seed 6)"
+    log(f"prefix cache: {res}")
+    return res
+
+
 def block_sweep(args, torch, np, api, driver, workloads, dev):
     """Decode at the Llama-3.1-8B shape for several block sizes with the same
     lengths and values (seed 2) and the same pool capacity (409,600 tokens
@@ -233,6 +264,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-copy-bandwidth", action="store_true")
     ap.add_argument("--no-swap", action="store_true")
+    ap.add_argument("--no-prefix-cache", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
@@ -386,6 +418,8 @@ def main():
 
     if not args.no_swap:
         result["swap"] = swap_leg(torch, api, dev)
+    if not args.no_prefix_cache:
+        result["prefix_cache"] = prefix_cache_leg(torch, np, api, driver, workloads, dev, 50, 5)
 
     pf = None
     if not args.no_prefill:

@@ -213,6 +213,32 @@ int pkv_seq_add(pkv_alloc* a, int64_t seq);
 int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t* copy_pairs_out,
                    int copy_cap, int* num_copies_out);
 
+/* Prefix caching: append n tokens whose ids are known (host int32
+ * tokens[n]).  cnblogs section 9: a prompt shared by many requests is stored
+ * once; "08. PagedAttention", section "what else paging solves": only full
+ * blocks are shared, by reference count.
+ * Every full block of a sequence whose appends all carried token ids is
+ * named by a chained hash: FNV-1a (64-bit) over the previous full block's
+ * hash (8 bytes little endian; 0 before the first block) followed by the
+ * block's token ids (4 bytes each, little endian).  A block this append
+ * covers whole, whose hash and token ids match a cached block, reuses that
+ * block (ref + 1; a cached block with count 0 is taken back off the free
+ * list) as long as every earlier new block of the append did too; its
+ * tokens get slot -1 in slots_out (their K/V are already in the cache:
+ * pkv_kv_write skips negative slots) and are counted in *num_cached_out.
+ * Hits are decided on the cache as it was before the call.  Other tokens
+ * are placed as pkv_seq_append places them, copy-on-write included.  A
+ * block filled by this append is filed under its hash unless the hash is
+ * cached already.  A block that leaves the free list for any other reason
+ * loses its cache entry.  A sequence that ever takes a plain pkv_seq_append
+ * (or was forked inside a block) no longer takes part.  Atomic like
+ * pkv_seq_append. */
+int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int n, int32_t* slots_out,
+                          int* num_cached_out, int32_t* copy_pairs_out, int copy_cap, int* num_copies_out);
+
+/* Number of blocks filed in the prefix cache. */
+int pkv_prefix_cache_size(const pkv_alloc* a, int* entries_out);
+
 /* child := first fork_pos tokens of parent, sharing its blocks.
  * PKV_ERR_INVALID for an unknown parent, an existing child or
  * fork_pos outside [0, len(parent)]. */

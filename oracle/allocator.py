@@ -46,10 +46,47 @@ PagedAttention", section "what it does not solve"):
 * ``swap_in`` takes as many fresh blocks off the free list as it had, in
   logical order (all or nothing); host buffer i goes to the i-th of them.
 * append, fork and table export refuse a swapped sequence; release drops it.
+
+Prefix caching (cnblogs section 9: a system prompt shared by many requests
+is stored once; "08. PagedAttention", section "what else paging solves":
+only full blocks are shared, through reference counts):
+
+* ``append_tokens`` names every full block of a sequence by a chained hash,
+  FNV-1a 64 over (previous full block's hash as 8 little-endian bytes, 0 for
+  the first block) followed by the block's token ids (4 little-endian bytes
+  each).
+* A block that the append covers whole reuses the cached block with the same
+  hash and tokens, while every earlier new block of the append did; hits are
+  decided on the cache as it stood before the append, and a hit block whose
+  count is 0 comes back off the free list.  Its tokens' slots are -1: there
+  is nothing to write.
+* Every other block is placed as ``append`` places it.  A block the append
+  filled is filed under its hash unless that hash is filed already.
+* A block taken off the free list loses its cache entry: it is about to be
+  overwritten.
+* A plain ``append`` (or a fork inside a block) takes the sequence out of
+  prefix caching for good.
 """
 from __future__ import annotations
 
 from typing import Dict, List, Optional, Sequence, Tuple
+
+FNV_OFFSET = 14695981039346656037
+FNV_PRIME = 1099511628211
+MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data: bytes, h: int = FNV_OFFSET) -> int:
+    """FNV-1a, 64 bit: for each byte, xor it in, then multiply by the prime."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
+
+
+def block_hash(prev: int, tokens: Sequence[int]) -> int:
+    data = prev.to_bytes(8, "little") + b"".join(int(t & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
 
 
 class OutOfBlocks(Exception):
@@ -75,6 +112,12 @@ class BlockAllocator:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.swapped: Dict[int, int] = {}  # seq -> table length when swapped out
+        # prefix caching
+        self.cache: Dict[int, int] = {}  # block hash -> block
+        self.cached_as: Dict[int, Tuple[int, Tuple[int, ...]]] = {}  # block -> (hash, token ids)
+        self.tok_ok: Dict[int, bool] = {}
+        self.hashes: Dict[int, List[int]] = {}  # seq -> hash of each full block
+        self.pending: Dict[int, List[int]] = {}  # seq -> token ids of the partial last block
 
     # -- sequence lifecycle -------------------------------------------------
     def add(self, seq: int) -> None:
@@ -82,9 +125,16 @@ class BlockAllocator:
             raise AllocatorError(f"sequence {seq} exists")
         self.tables[seq] = []
         self.lens[seq] = 0
+        self.tok_ok[seq] = True
+        self.hashes[seq] = []
+        self.pending[seq] = []
 
     def _pop(self) -> int:
-        return self.free.pop()
+        b = self.free.pop()
+        if b in self.cached_as:  # its contents are about to be overwritten
+            h, _ = self.cached_as.pop(b)
+            del self.cache[h]
+        return b
 
     def append(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
         """Reserve slots for ``n`` new tokens of ``seq``.  Returns the slot of
@@ -114,6 +164,9 @@ class BlockAllocator:
                 need += 1
         if need > len(self.free):
             raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        if n > 0:
+            self.tok_ok[seq] = False
+            self.pending[seq] = []
         slots: List[int] = []
         copies: List[Tuple[int, int]] = []
         for p in range(start, start + n):
@@ -148,6 +201,11 @@ class BlockAllocator:
             self.ref[b] += 1
         self.tables[child] = list(shared)
         self.lens[child] = fork_pos
+        whole = fork_pos // self.block_size
+        ok = self.tok_ok[parent] and fork_pos % self.block_size == 0 and len(self.hashes[parent]) >= whole
+        self.tok_ok[child] = ok
+        self.hashes[child] = list(self.hashes[parent][:whole]) if ok else []
+        self.pending[child] = []
 
     def _give_back(self, table: List[int]) -> None:
         for b in reversed(table):
@@ -165,6 +223,8 @@ class BlockAllocator:
         del self.tables[seq]
         del self.lens[seq]
         self.swapped.pop(seq, None)
+        for d in (self.tok_ok, self.hashes, self.pending):
+            d.pop(seq, None)
 
     def swap_out(self, seq: int) -> List[int]:
         if seq not in self.tables:
@@ -183,12 +243,87 @@ class BlockAllocator:
         n = self.swapped[seq]
         if n > len(self.free):
             raise OutOfBlocks(f"need {n} blocks, {len(self.free)} free")
-        table = [self._pop() for _ in range(n)]
-        for b in table:
+        table = []
+        for _ in range(n):
+            b = self._pop()
             self.ref[b] = 1
+            table.append(b)
         self.tables[seq] = table
         del self.swapped[seq]
         return list(table)
+
+    def append_tokens(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]], int]:
+        """Append tokens with known ids; returns (slots with -1 for cached
+        tokens, copies, number of cached tokens)."""
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise AllocatorError(f"sequence {seq} is swapped out")
+        tokens = [int(t) for t in tokens]
+        if not self.tok_ok[seq]:
+            slots, copies = self.append(seq, len(tokens))
+            return slots, copies, 0
+        B = self.block_size
+        table = self.tables[seq]
+        start = self.lens[seq]
+        n = len(tokens)
+        end = start + n
+        have = len(table)
+        # the blocks that become full, their hashes, and the hits (decided
+        # on the cache as it is now)
+        filled = []  # (logical block, hash, token ids)
+        hit: Dict[int, int] = {}
+        cur = list(self.pending[seq])
+        prev = self.hashes[seq][-1] if self.hashes[seq] else 0
+        chain = True
+        for p in range(start, end):
+            cur.append(tokens[p - start])
+            if len(cur) == B:
+                lb = p // B
+                h = block_hash(prev, cur)
+                filled.append((lb, h, tuple(cur)))
+                if lb >= have:
+                    b = self.cache.get(h) if chain else None
+                    if b is not None and self.cached_as[b][1] == tuple(cur):
+                        hit[lb] = b
+                    else:
+                        chain = False
+                prev = h
+                cur = []
+        # blocks the free list has to give
+        cow = n > 0 and start // B < have and self.ref[table[start // B]] > 1
+        want = -(-end // B)
+        need = int(cow) + sum(1 for lb in range(have, want) if lb not in hit or self.ref[hit[lb]] == 0)
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        for lb in range(have, want):
+            if lb in hit and self.ref[hit[lb]] == 0:
+                self.free.remove(hit[lb])
+        copies: List[Tuple[int, int]] = []
+        if cow:
+            old = table[start // B]
+            b = self._pop()
+            copies.append((old, b))
+            self.ref[old] -= 1
+            self.ref[b] = 1
+            table[start // B] = b
+        for lb in range(have, want):
+            if lb in hit:
+                b = hit[lb]
+                self.ref[b] += 1
+            else:
+                b = self._pop()
+                self.ref[b] = 1
+            table.append(b)
+        slots = [-1 if (p // B) in hit else table[p // B] * B + p % B for p in range(start, end)]
+        for lb, h, toks in filled:
+            self.hashes[seq].append(h)
+            if lb not in hit and h not in self.cache:
+                self.cache[h] = table[lb]
+                self.cached_as[table[lb]] = (h, toks)
+        self.pending[seq] = cur
+        self.lens[seq] = end
+        return slots, copies, sum(1 for s in slots if s < 0)
 
     # -- queries ------------------------------------------------------------
     def table(self, seq: int) -> List[int]:

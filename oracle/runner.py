@@ -43,7 +43,10 @@ def run(wl, with_pools: bool = True) -> OracleState:
             if op.kind == "add":
                 alloc.add(op.seq)
             elif op.kind == "append":
-                sl, cp = alloc.append(op.seq, op.n)
+                if op.tokens is not None:
+                    sl, cp, _ = alloc.append_tokens(op.seq, op.tokens)
+                else:
+                    sl, cp = alloc.append(op.seq, op.n)
                 slots += sl
                 copies += cp
                 if op.k is not None:

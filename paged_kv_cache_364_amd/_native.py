@@ -64,6 +64,8 @@ SIGNATURES = {
     "pkv_alloc_destroy": (None, [vp]),
     "pkv_seq_add": (c_int, [vp, c_i64]),
     "pkv_seq_append": (c_int, [vp, c_i64, c_int, i32p, i32p, c_int, intp]),
+    "pkv_seq_append_tokens": (c_int, [vp, c_i64, i32p, c_int, i32p, intp, i32p, c_int, intp]),
+    "pkv_prefix_cache_size": (c_int, [vp, intp]),
     "pkv_seq_fork": (c_int, [vp, c_i64, c_i64, c_int]),
     "pkv_seq_free": (c_int, [vp, c_i64]),
     "pkv_seq_swap_out": (c_int, [vp, c_i64, i32p, c_int, intp]),

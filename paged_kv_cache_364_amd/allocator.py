@@ -56,6 +56,28 @@ class BlockAllocator:
         N.check(st, "seq_append")
         return slots[: int(n)], [(int(pairs[0]), int(pairs[1]))] if nc.value else []
 
+    def append_tokens(self, seq: int, tokens) -> Tuple[np.ndarray, List[Tuple[int, int]], int]:
+        """Append tokens with known ids, reusing cached full blocks
+        (pkv_seq_append_tokens).  Returns slots (-1 where the token's K/V
+        are already cached), copies, and the number of cached tokens."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = tok.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty(2, dtype=np.int32)
+        nc, ncached = ctypes.c_int(0), ctypes.c_int(0)
+        st = self._L.pkv_seq_append_tokens(self._h, int(seq), tok.ctypes.data_as(N.i32p), n,
+                                           slots.ctypes.data_as(N.i32p), ctypes.byref(ncached),
+                                           pairs.ctypes.data_as(N.i32p), 1, ctypes.byref(nc))
+        if st == N.PKV_ERR_NO_BLOCKS:
+            raise OutOfBlocks(st, "seq_append_tokens")
+        N.check(st, "seq_append_tokens")
+        return slots[:n], ([(int(pairs[0]), int(pairs[1]))] if nc.value else []), int(ncached.value)
+
+    def prefix_cache_size(self) -> int:
+        x = ctypes.c_int(0)
+        N.check(self._L.pkv_prefix_cache_size(self._h, ctypes.byref(x)), "prefix_cache_size")
+        return int(x.value)
+
     def fork(self, parent: int, child: int, fork_pos: int) -> None:
         N.check(self._L.pkv_seq_fork(self._h, int(parent), int(child), int(fork_pos)), "seq_fork")
 

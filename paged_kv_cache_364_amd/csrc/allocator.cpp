@@ -22,8 +22,22 @@
 // swapped-out sequence gives its blocks back exactly as a release would,
 // keeps its length, and holds no blocks until it is swapped in, which takes
 // fresh blocks off the free list in logical order (all-or-nothing).
+//
+// Prefix caching (cnblogs section 9: a shared system prompt is stored once;
+// "08. PagedAttention", section "what else paging solves": only full blocks
+// are shared, by reference count): appends that carry token ids name each
+// full block by a chained FNV-1a hash of (previous block's hash, the block's
+// token ids).  A block the append covers whole whose hash, and tokens, match
+// a cached block reuses it (ref + 1, taken back off the free list if its
+// count was 0) and its tokens get slot -1 (nothing to write).  Hits are
+// decided for the whole append before anything is popped; a block that
+// becomes full is registered unless its hash is already cached; a block
+// popped off the free list loses its cache entry (its contents are about to
+// be overwritten).
 #include <stdint.h>
+#include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -36,13 +50,62 @@ struct pkv_alloc {
     int64_t len = 0;
     bool swapped = false;
     int64_t swapped_blocks = 0;  // table length when it was swapped out
+    // prefix caching: every append so far carried token ids
+    bool tok_ok = true;
+    std::vector<uint64_t> hashes;  // chained hash of each full block
+    std::vector<int32_t> pending;  // token ids of the partial last block
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::vector<int32_t> free_stack;  // back() is the top
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<uint64_t, int32_t> cache;        // block hash -> block
+  std::vector<uint64_t> block_hash;                   // hash a cached block is filed under
+  std::vector<char> block_cached;                     // block has a cache entry
+  std::vector<std::vector<int32_t>> block_tokens;     // token ids of a cached block
 };
+
+namespace {
+
+// FNV-1a, 64 bit: offset basis 14695981039346656037, prime 1099511628211.
+uint64_t fnv1a(uint64_t h, const unsigned char* p, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+// Hash of a full block: FNV-1a over the previous block's hash (8 bytes,
+// little endian) followed by the block's token ids (4 bytes each, little
+// endian); the first block's previous hash is 0.
+uint64_t block_hash_of(uint64_t prev, const int32_t* tokens, int B) {
+  unsigned char buf[8];
+  for (int i = 0; i < 8; ++i) buf[i] = (unsigned char)(prev >> (8 * i));
+  uint64_t h = fnv1a(14695981039346656037ull, buf, 8);
+  for (int j = 0; j < B; ++j) {
+    const uint32_t t = (uint32_t)tokens[j];
+    unsigned char b4[4] = {(unsigned char)t, (unsigned char)(t >> 8), (unsigned char)(t >> 16),
+                           (unsigned char)(t >> 24)};
+    h = fnv1a(h, b4, 4);
+  }
+  return h;
+}
+
+// Pop the top of the free stack; the block's cache entry, if any, goes.
+int32_t pop_block(pkv_alloc* a) {
+  const int32_t b = a->free_stack.back();
+  a->free_stack.pop_back();
+  if (a->block_cached[(size_t)b]) {
+    a->cache.erase(a->block_hash[(size_t)b]);
+    a->block_cached[(size_t)b] = 0;
+    a->block_tokens[(size_t)b].clear();
+  }
+  return b;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -54,6 +117,9 @@ pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* init_
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->ref.assign((size_t)num_blocks, 0);
+    a->block_hash.assign((size_t)num_blocks, 0);
+    a->block_cached.assign((size_t)num_blocks, 0);
+    a->block_tokens.resize((size_t)num_blocks);
     a->free_stack.resize((size_t)num_blocks);
     std::vector<char> seen((size_t)num_blocks, 0);
     for (int i = 0; i < num_blocks; ++i) {
@@ -113,17 +179,19 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
     return PKV_ERR_STATE;
   }
   int nc = 0;
+  if (n > 0) {
+    s.tok_ok = false;
+    s.pending.clear();
+  }
   for (int64_t p = start; p < end; ++p) {
     const int64_t lb = p / B;
     if (lb == (int64_t)s.table.size()) {
-      const int32_t b = a->free_stack.back();
-      a->free_stack.pop_back();
+      const int32_t b = pop_block(a);
       a->ref[(size_t)b] = 1;
       s.table.push_back(b);
     } else if (a->ref[(size_t)s.table[(size_t)lb]] > 1) {
       const int32_t old = s.table[(size_t)lb];
-      const int32_t b = a->free_stack.back();
-      a->free_stack.pop_back();
+      const int32_t b = pop_block(a);
       copy_pairs_out[2 * nc] = old;
       copy_pairs_out[2 * nc + 1] = b;
       ++nc;
@@ -138,6 +206,153 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
   return PKV_OK;
 }
 
+int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int n, int32_t* slots_out,
+                          int* num_cached_out, int32_t* copy_pairs_out, int copy_cap, int* num_copies_out) {
+  if (!a || n < 0 || (n > 0 && (!slots_out || !tokens))) return PKV_ERR_INVALID;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_ERR_INVALID;
+  pkv_alloc::Seq& s = it->second;
+  if (s.swapped) return PKV_ERR_STATE;
+  if (!s.tok_ok) {  // no hash chain (an earlier append carried no tokens): no caching
+    const int st = pkv_seq_append(a, seq, n, slots_out, copy_pairs_out, copy_cap, num_copies_out);
+    if (st == PKV_OK && num_cached_out) *num_cached_out = 0;
+    return st;
+  }
+  const int64_t B = a->block_size;
+  const int64_t start = s.len;
+  const int64_t end = start + n;
+  const int64_t have = (int64_t)s.table.size();
+  const int64_t first = start / B;
+  const int64_t want = (end + B - 1) / B;
+  const int64_t nb = want > first ? want - first : 0;
+  // 1. hashes of the blocks that become full, and hits, decided on the
+  //    cache as it is before this append: a block past the table (so
+  //    covered whole by the append) hits if a cached block carries its hash
+  //    and tokens, as long as every earlier new block of the append hit
+  std::vector<uint64_t> hsh;
+  std::vector<int32_t> hit;
+  std::vector<char> full;
+  std::vector<int32_t> cur;
+  try {
+    hsh.assign((size_t)nb, 0);
+    hit.assign((size_t)nb, -1);
+    full.assign((size_t)nb, 0);
+    cur = s.pending;
+    uint64_t prev = s.hashes.empty() ? 0 : s.hashes.back();
+    bool chain = true;
+    for (int64_t p = start; p < end; ++p) {
+      cur.push_back(tokens[p - start]);
+      if ((int64_t)cur.size() == B) {
+        const int64_t lb = p / B;
+        const size_t i = (size_t)(lb - first);
+        const uint64_t h = block_hash_of(prev, cur.data(), (int)B);
+        hsh[i] = h;
+        full[i] = 1;
+        if (lb >= have) {
+          if (chain) {
+            auto c = a->cache.find(h);
+            if (c != a->cache.end() &&
+                memcmp(a->block_tokens[(size_t)c->second].data(), cur.data(), (size_t)B * sizeof(int32_t)) == 0)
+              hit[i] = c->second;
+          }
+          if (hit[i] < 0) chain = false;
+        }
+        prev = h;
+        cur.clear();
+      }
+    }
+  } catch (...) {
+    return PKV_ERR_STATE;
+  }
+  // 2. blocks taken off the free list: the copy of a shared partial block,
+  //    every new block that misses, and hits whose count is 0
+  int64_t need = 0;
+  const bool cow = n > 0 && first < have && a->ref[(size_t)s.table[(size_t)first]] > 1;
+  if (cow) ++need;
+  for (int64_t lb = std::max(first, have); lb < want; ++lb) {
+    const int32_t hb = hit[(size_t)(lb - first)];
+    if (hb < 0 || a->ref[(size_t)hb] == 0) ++need;
+  }
+  if (cow && (copy_cap < 1 || !copy_pairs_out)) return PKV_ERR_INVALID;
+  if (need > (int64_t)a->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+  try {
+    s.table.reserve((size_t)want);
+    s.hashes.reserve(s.hashes.size() + (size_t)nb);
+  } catch (...) {
+    return PKV_ERR_STATE;
+  }
+  // 3. hits with count 0 leave the free list before anything is popped
+  for (int64_t lb = std::max(first, have); lb < want; ++lb) {
+    const int32_t hb = hit[(size_t)(lb - first)];
+    if (hb >= 0 && a->ref[(size_t)hb] == 0)
+      a->free_stack.erase(std::find(a->free_stack.begin(), a->free_stack.end(), hb));
+  }
+  // 4. as a plain append: the copy first, then new blocks in logical order
+  int nc = 0;
+  if (cow) {
+    const int32_t old = s.table[(size_t)first];
+    const int32_t b = pop_block(a);
+    copy_pairs_out[0] = old;
+    copy_pairs_out[1] = b;
+    nc = 1;
+    a->ref[(size_t)old] -= 1;
+    a->ref[(size_t)b] = 1;
+    s.table[(size_t)first] = b;
+  }
+  for (int64_t lb = std::max(first, have); lb < want; ++lb) {
+    const int32_t hb = hit[(size_t)(lb - first)];
+    if (hb >= 0) {
+      a->ref[(size_t)hb] += 1;
+      s.table.push_back(hb);
+    } else {
+      const int32_t b = pop_block(a);
+      a->ref[(size_t)b] = 1;
+      s.table.push_back(b);
+    }
+  }
+  // 5. slots (-1 for tokens already in a cached block), hash chain, and
+  //    registration of the blocks this append filled
+  int ncached = 0;
+  for (int64_t p = start; p < end; ++p) {
+    const int64_t lb = p / B;
+    if (hit[(size_t)(lb - first)] >= 0) {
+      slots_out[p - start] = -1;
+      ++ncached;
+    } else {
+      slots_out[p - start] = (int32_t)(s.table[(size_t)lb] * B + p % B);
+    }
+  }
+  std::vector<int32_t> blk_tokens;
+  blk_tokens = s.pending;
+  for (int64_t p = start; p < end; ++p) {
+    blk_tokens.push_back(tokens[p - start]);
+    if ((int64_t)blk_tokens.size() == B) {
+      const int64_t lb = p / B;
+      const size_t i = (size_t)(lb - first);
+      const int32_t blk = s.table[(size_t)lb];
+      s.hashes.push_back(hsh[i]);
+      if (hit[i] < 0 && !a->cache.count(hsh[i])) {
+        a->cache.emplace(hsh[i], blk);
+        a->block_hash[(size_t)blk] = hsh[i];
+        a->block_cached[(size_t)blk] = 1;
+        a->block_tokens[(size_t)blk] = blk_tokens;
+      }
+      blk_tokens.clear();
+    }
+  }
+  s.pending = blk_tokens;
+  s.len = end;
+  if (num_copies_out) *num_copies_out = nc;
+  if (num_cached_out) *num_cached_out = ncached;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_size(const pkv_alloc* a, int* entries_out) {
+  if (!a || !entries_out) return PKV_ERR_INVALID;
+  *entries_out = (int)a->cache.size();
+  return PKV_OK;
+}
+
 int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos) {
   if (!a) return PKV_ERR_INVALID;
   auto it = a->seqs.find(parent);
@@ -149,6 +364,12 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos) {
   try {
     c.table.assign(it->second.table.begin(), it->second.table.begin() + nb);
     c.len = fork_pos;
+    // a child forked on a block boundary inherits the hash chain; one forked
+    // inside a block does not take part in prefix caching
+    const pkv_alloc::Seq& par = it->second;
+    c.tok_ok = par.tok_ok && fork_pos % a->block_size == 0 &&
+               (int64_t)par.hashes.size() >= fork_pos / a->block_size;
+    if (c.tok_ok) c.hashes.assign(par.hashes.begin(), par.hashes.begin() + fork_pos / a->block_size);
     for (int32_t b : c.table) a->ref[(size_t)b] += 1;
     a->seqs.emplace(child, std::move(c));
   } catch (...) {
@@ -208,8 +429,7 @@ int pkv_seq_swap_in(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int
     return PKV_ERR_STATE;
   }
   for (int64_t i = 0; i < n; ++i) {
-    const int32_t b = a->free_stack.back();
-    a->free_stack.pop_back();
+    const int32_t b = pop_block(a);
     a->ref[(size_t)b] = 1;
     s.table.push_back(b);
     blocks_out[i] = b;

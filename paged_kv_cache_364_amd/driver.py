@@ -69,7 +69,10 @@ def run_script(wl, device="cuda", pools: Optional[tuple] = None) -> GpuState:
             if op.kind == "add":
                 alloc.add(op.seq)
             elif op.kind == "append":
-                sl, cp = alloc.append(op.seq, op.n)
+                if op.tokens is not None:
+                    sl, cp, _ = alloc.append_tokens(op.seq, op.tokens)
+                else:
+                    sl, cp = alloc.append(op.seq, op.n)
                 sl = sl.tolist()
                 slots += sl
                 copies += cp

@@ -70,6 +70,7 @@ class Op:
     fork_pos: int = 0
     k: Optional[np.ndarray] = None
     v: Optional[np.ndarray] = None
+    tokens: Optional[np.ndarray] = None  # token ids: the append goes through the prefix cache
 
 
 @dataclass
@@ -361,6 +362,44 @@ def prefill_workload(seed=5, num_seqs=16, prefix_hi=1536, chunk=512, num_blocks=
 
 def config5():
     return prefill_workload(5, 16, 1536, 512, 4096, OPT13B, "opt13b-prefill-b16x512")
+
+
+def shared_prompt_requests(seed=6, num_requests=16, prompt_len=1000, suffix_hi=200, num_blocks=4096,
+                           block_size=16, vocab=32000, use_cache=True, name=None):
+    """Requests that share a system prompt (cnblogs section 9): request r is
+    the prompt followed by its own suffix of U{1..suffix_hi} tokens, then one
+    decode token.  A token's K/V depend only on the token ids up to it, so
+    the prompt's K/V are drawn once and every request carries the same rows
+    for it.  With ``use_cache`` the appends carry token ids (prefix caching);
+    without, the same script uses plain appends."""
+    rng = np.random.default_rng(seed)
+    hkv, d = LLAMA["num_kv_heads"], LLAMA["head_dim"]
+    suffix = rng.integers(1, suffix_hi + 1, size=num_requests)
+    init_order = rng.permutation(num_blocks).astype(np.int32)
+    q = _values(rng, (num_requests, LLAMA["num_heads"], d), BF16)
+    prompt_tok = rng.integers(0, vocab, size=prompt_len).astype(np.int32)
+    kp = _values(rng, (prompt_len, hkv, d), BF16)
+    vp = _values(rng, (prompt_len, hkv, d), BF16)
+    tot = int(suffix.sum())
+    sfx_tok = rng.integers(0, vocab, size=tot + num_requests).astype(np.int32)
+    ks = _values(rng, (tot, hkv, d), BF16)
+    vs = _values(rng, (tot, hkv, d), BF16)
+    kn = _values(rng, (num_requests, hkv, d), BF16)
+    vn = _values(rng, (num_requests, hkv, d), BF16)
+    a = Step()
+    off = 0
+    for r in range(num_requests):
+        n = int(suffix[r])
+        toks = np.concatenate([prompt_tok, sfx_tok[off: off + n]])
+        a.ops += [Op("add", r), Op("append", r, n=prompt_len + n, k=np.concatenate([kp, ks[off: off + n]]),
+                                   v=np.concatenate([vp, vs[off: off + n]]), tokens=toks if use_cache else None)]
+        off += n
+    b = Step([Op("append", r, n=1, k=kn[r: r + 1], v=vn[r: r + 1],
+                 tokens=sfx_tok[tot + r: tot + r + 1] if use_cache else None) for r in range(num_requests)])
+    mb = -(-(prompt_len + suffix_hi + 1) // block_size)
+    return Workload(name or f"llama31-8b-shared-prompt-{num_requests}x{prompt_len}", "decode", BF16, **LLAMA,
+                    block_size=block_size, num_blocks=num_blocks, scale=_scale(d), init_order=init_order,
+                    steps=[a, b], batch=list(range(num_requests)), q=q, max_blocks_per_seq=mb)
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}

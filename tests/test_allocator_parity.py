@@ -26,6 +26,7 @@ def same_state(a: BlockAllocator, o: OracleAlloc):
     assert st.num_shared == sum(1 for r in o.ref if r > 1)
     assert st.logical_tokens == sum(o.lens.values())
     assert st.table_slots == sum(len(t) for t in o.tables.values()) * o.block_size
+    assert a.prefix_cache_size() == len(o.cache)
 
 
 def run_both(wl):
@@ -36,6 +37,10 @@ def run_both(wl):
             if op.kind == "add":
                 a.add(op.seq)
                 o.add(op.seq)
+            elif op.kind == "append" and op.tokens is not None:
+                s1, c1, n1 = a.append_tokens(op.seq, op.tokens)
+                s2, c2, n2 = o.append_tokens(op.seq, op.tokens)
+                assert s1.tolist() == s2 and c1 == c2 and n1 == n2
             elif op.kind == "append":
                 s1, c1 = a.append(op.seq, op.n)
                 s2, c2 = o.append(op.seq, op.n)
@@ -62,6 +67,8 @@ def test_shrunk_workloads():
     run_both(W.ragged_decode(3, 32, 2048, 400, hi=1024))
     run_both(W.shared_prefix(4, 3, 1024, 4, fork_points=[1000, 1008, 1023], priv_hi=40, num_blocks=1024))
     run_both(W.prefill_workload(5, 4, 100, 37, 256))
+    run_both(W.shared_prompt_requests(6, 6, 100, 30, 256, block_size=16))
+    run_both(W.shared_prompt_requests(7, 5, 45, 9, 128, block_size=8))
 
 
 @pytest.mark.slow
@@ -104,6 +111,84 @@ def test_random_ops_match():
                 live.append(nxt)
                 nxt += 1
             elif r < 0.78:
+                s = live.pop(rng.integers(len(live)))
+                assert a.swap_out(s) == o.swap_out(s)
+                swapped.append(s)
+            elif r < 0.88 and swapped:
+                s = swapped[rng.integers(len(swapped))]
+                try:
+                    t2 = o.swap_in(s)
+                except OracleOOB:
+                    with pytest.raises(OutOfBlocks):
+                        a.swap_in(s)
+                else:
+                    assert a.swap_in(s) == t2
+                    swapped.remove(s)
+                    live.append(s)
+            else:
+                pool = live + swapped
+                s = pool[rng.integers(len(pool))]
+                a.release(s)
+                o.release(s)
+                (live if s in live else swapped).remove(s)
+            same_state(a, o)
+
+
+def test_random_prefix_cache_ops_match():
+    """Sequences that follow a few shared documents, so that full blocks
+    repeat; appends with token ids, plain appends, forks, swaps, releases."""
+    for seed in range(6):
+        rng = np.random.default_rng(300 + seed)
+        N, B = 48, [2, 4, 8][seed % 3]
+        order = rng.permutation(N)
+        a = BlockAllocator(N, B, order)
+        o = OracleAlloc(N, B, order)
+        docs = [rng.integers(0, 5, size=200).astype(np.int32) for _ in range(3)]
+        doc_of, live, swapped, nxt = {}, [], [], 0
+        for _ in range(250):
+            r = rng.random()
+            if r < 0.2 or not live:
+                a.add(nxt)
+                o.add(nxt)
+                doc_of[nxt] = int(rng.integers(len(docs)))
+                live.append(nxt)
+                nxt += 1
+            elif r < 0.6:
+                s = live[rng.integers(len(live))]
+                pos = o.length(s)
+                k = int(rng.integers(0, 3 * B))
+                toks = docs[doc_of[s]][pos: pos + k]
+                if len(toks) < k:
+                    toks = np.concatenate([toks, rng.integers(0, 5, size=k - len(toks)).astype(np.int32)])
+                try:
+                    s2, c2, n2 = o.append_tokens(s, toks)
+                except OracleOOB:
+                    with pytest.raises(OutOfBlocks):
+                        a.append_tokens(s, toks)
+                else:
+                    s1, c1, n1 = a.append_tokens(s, toks)
+                    assert s1.tolist() == s2 and c1 == c2 and n1 == n2
+            elif r < 0.65:
+                s = live[rng.integers(len(live))]
+                try:
+                    s2, c2 = o.append(s, 1)
+                except OracleOOB:
+                    with pytest.raises(OutOfBlocks):
+                        a.append(s, 1)
+                else:
+                    s1, c1 = a.append(s, 1)
+                    assert s1.tolist() == s2 and c1 == c2
+            elif r < 0.75:
+                s = live[rng.integers(len(live))]
+                f = int(rng.integers(0, o.length(s) + 1))
+                if rng.random() < 0.5:
+                    f -= f % B
+                a.fork(s, nxt, f)
+                o.fork(s, nxt, f)
+                doc_of[nxt] = doc_of[s]
+                live.append(nxt)
+                nxt += 1
+            elif r < 0.82:
                 s = live.pop(rng.integers(len(live)))
                 assert a.swap_out(s) == o.swap_out(s)
                 swapped.append(s)

@@ -199,3 +199,18 @@ def test_swap_out_keeping_blocks_is_caught(monkeypatch):
 
     monkeypatch.setattr(BlockAllocator, "swap_out", swap_out_without_release)
     assert fails(P.check_swap_allocator)
+
+
+def test_unchained_block_hash_is_caught(monkeypatch):
+    import oracle.allocator as A
+    real = A.block_hash
+    monkeypatch.setattr(A, "block_hash", lambda prev, toks: real(0, toks))
+    assert fails(P.check_prefix_cache)
+
+
+def test_block_hash_over_part_of_the_block_is_caught(monkeypatch):
+    """A hash that skips the chain and the block's first token."""
+    import oracle.allocator as A
+    real = A.block_hash
+    monkeypatch.setattr(A, "block_hash", lambda prev, toks: real(0, toks[1:]))
+    assert fails(P.check_prefix_cache)

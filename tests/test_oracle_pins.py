@@ -582,3 +582,96 @@ def check_swap_roundtrip():
 
 def test_swap_roundtrip():
     check_swap_roundtrip()
+
+
+# ---------------------------------------------------------------------------
+# prefix caching (cnblogs section 9; "08. PagedAttention", "what else paging solves")
+# ---------------------------------------------------------------------------
+def test_fnv1a_published_vectors():
+    """FNV-1a 64-bit test vectors from the algorithm's published reference."""
+    from oracle.allocator import fnv1a64
+    assert fnv1a64(b"") == 0xCBF29CE484222325
+    assert fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def check_prefix_cache():
+    B = 4
+    a = BlockAllocator(16, B)
+    prompt = [11, 12, 13, 14, 21, 22, 23, 24, 31, 32]
+    a.add(0)
+    s0, _, c0 = a.append_tokens(0, prompt)
+    assert c0 == 0 and s0 == [b * B + o for b in a.table(0) for o in range(B)][:10]
+    assert len(a.cache) == 2  # two full blocks filed; the partial third is not
+    a.add(1)
+    s1, _, c1 = a.append_tokens(1, prompt)
+    assert c1 == 8 and s1[:8] == [-1] * 8  # blocks 0 and 1 reused, nothing to write
+    assert a.table(1)[:2] == a.table(0)[:2] and a.table(1)[2] != a.table(0)[2]
+    assert all(a.ref[b] == 2 for b in a.table(0)[:2])
+    # same second block, different first block: the chain keeps them apart
+    a.add(2)
+    _, _, c2 = a.append_tokens(2, [99, 12, 13, 14, 21, 22, 23, 24])
+    assert c2 == 0
+    # a changed token in block 1 stops the hits at block 0
+    a.add(3)
+    s3, _, c3 = a.append_tokens(3, [11, 12, 13, 14, 21, 22, 0, 24, 31])
+    assert c3 == 4 and s3[:4] == [-1] * 4 and s3[4] >= 0
+    # released blocks stay cached on the free list and come back off it
+    b01 = a.table(0)[:2]
+    for s in (0, 1, 3):
+        a.release(s)
+    assert all(b in a.free for b in b01[1:])
+    a.add(4)
+    _, _, c4 = a.append_tokens(4, prompt + [41, 42])
+    assert c4 == 8 and a.table(4)[:2] == b01 and not any(b in a.free for b in b01)
+    allocator_invariants(a)
+    # the filled third block (31, 32, 41, 42) is now cached too
+    a.add(5)
+    _, _, c5 = a.append_tokens(5, prompt + [41, 42])
+    assert c5 == 12
+    # a block with cached tokens but another prefix is not a hit
+    a.add(9)
+    a.append_tokens(9, [1, 2, 3, 4])
+    _, _, c9 = a.append_tokens(9, [21, 22, 23, 24])
+    assert c9 == 0
+    a.release(9)
+    # eviction: blocks popped off the free list leave the cache
+    for s in (4, 5):
+        a.release(s)
+    a.add(6)
+    a.append(6, B * len(a.free))  # takes every free block, cached ones included
+    a.release(6)
+    a.add(7)
+    _, _, c7 = a.append_tokens(7, prompt)
+    assert c7 == 0
+    # a plain append takes a sequence out of prefix caching
+    a.add(8)
+    a.append(8, 1)
+    _, _, c8 = a.append_tokens(8, prompt[1:9])
+    assert c8 == 0
+
+
+def test_prefix_cache():
+    check_prefix_cache()
+
+
+def check_prefix_cache_attention():
+    """Requests sharing a system prompt, with the prefix cache and without:
+    fewer blocks, the prompt's K/V written once, attention bitwise equal."""
+    kw = dict(seed=61, num_requests=5, prompt_len=45, suffix_hi=9, num_blocks=256, block_size=8)
+    wl_c = W.shared_prompt_requests(**kw, use_cache=True)
+    wl_p = W.shared_prompt_requests(**kw, use_cache=False)
+    st_c, st_p = runner.run(wl_c), runner.run(wl_p)
+    o_c, o_p = runner.expected(wl_c, st_c), runner.expected(wl_p, st_p)
+    assert np.array_equal(o_c, o_p)
+    used_c = sum(1 for r in st_c.alloc.ref if r > 0)
+    used_p = sum(1 for r in st_p.alloc.ref if r > 0)
+    assert used_p - used_c == 4 * (45 // 8)  # requests 1..4 reuse the prompt's 5 full blocks
+    # request 0 writes all its tokens; requests 1..4 skip the prompt's 40 cached tokens
+    written = sum(1 for s in st_c.step_slots[0] if s >= 0)
+    total = sum(len(op.k) for op in wl_c.steps[0].ops if op.kind == "append")
+    assert written == total - 4 * 40
+
+
+def test_prefix_cache_attention():
+    check_prefix_cache_attention()
