@@ -212,6 +212,39 @@ def prefix_cache_leg(torch, np, api, driver, workloads, dev, steps, warmup):
     return res
 
 
+def window_leg(torch, np, api, driver, workloads, dev, steps, warmup, window=512):
+    """Config 2's batch with a sliding window of `window` tokens: blocks
+    wholly before each window released (pkv_seq_trim), decode over the
+    trimmed tables; GB/s over the K/V bytes the window holds."""
+    wl = workloads.config2()
+    st = driver.run_script(wl, device=dev)
+    a = st.alloc
+    used_before = a.stats().num_used
+    freed = sum(a.trim(s, max(0, a.length(s) - window)) for s in wl.batch)
+    tables, lens = a.block_tables(wl.batch, wl.max_blocks_per_seq)
+    tables_dev, lens_dev = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    q = driver.to_device(wl.q, wl.dtype, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                                               wl.block_size, wl.max_blocks_per_seq, q.dtype),
+                     dtype=torch.uint8, device=dev)
+
+    def decode(i):
+        api.paged_attention_decode(out, q, st.k_pool, st.v_pool, tables_dev, lens_dev, float(wl.scale),
+                                   workspace=ws, window=window)
+
+    ms, _ = timed_calls(torch, decode, steps, warmup, stream=torch.cuda.current_stream())
+    kv = int(np.minimum(lens.astype(np.int64), window).sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    res = {"window": window, "blocks_released": int(freed), "blocks_held": int(a.stats().num_used),
+           "blocks_held_full": int(used_before), "decode_us_avg": round(ms * 1e3, 2),
+           "window_kv_gbps": round(kv / (ms * 1e-3) / 1e9, 1),
+           "note": "one layer, not rotated: the window's K/V may sit in the Infinity Cache"}
+    log(f"sliding window: {res}")
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
 def block_sweep(args, torch, np, api, driver, workloads, dev):
     """Decode at the Llama-3.1-8B shape for several block sizes with the same
     lengths and values (seed 2) and the same pool capacity (409,600 tokens
@@ -265,6 +298,7 @@ def main():
     ap.add_argument("--no-copy-bandwidth", action="store_true")
     ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--no-prefix-cache", action="store_true")
+    ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
@@ -418,6 +452,8 @@ def main():
 
     if not args.no_swap:
         result["swap"] = swap_leg(torch, api, dev)
+    if not args.no_window:
+        result["sliding_window"] = window_leg(torch, np, api, driver, workloads, dev, 50, 5)
     if not args.no_prefix_cache:
         result["prefix_cache"] = prefix_cache_leg(torch, np, api, driver, workloads, dev, 50, 5)
 

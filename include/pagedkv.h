@@ -147,6 +147,19 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                float scale, int dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Sliding-window decode: as pkv_paged_attention_decode, but sequence s
+ * attends only its last min(window, context_lens[s]) tokens (streaming with
+ * a sliding window whose old blocks are reclaimed: intelliparadigm.com
+ * article, section 5.2).  Table entries of blocks that lie wholly before
+ * the window are never read, so pkv_seq_trim may have released them (-1).
+ * window must be > 0 (PKV_ERR_INVALID otherwise); the workspace is sized by
+ * pkv_decode_workspace_size as for the full decode. */
+int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks, int window, float scale,
+                                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * paged_attention_prefill: a causal query chunk over a cached prefix.
  * Query i of sequence s (rows cu_q_lens[s] .. cu_q_lens[s+1]-1 of q) sits at
@@ -235,6 +248,17 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
  * pkv_seq_append. */
 int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int n, int32_t* slots_out,
                           int* num_cached_out, int32_t* copy_pairs_out, int copy_cap, int* num_copies_out);
+
+/* Sliding-window reclamation (intelliparadigm.com article, section 5.2):
+ * release every block of the sequence that lies wholly before position
+ * keep_from (logical blocks lb with (lb + 1) * block_size <= keep_from),
+ * last first, as pkv_seq_free would; their table entries become -1 (a hole
+ * that no kernel reads) and the length is unchanged.  *freed_out counts the
+ * entries released by this call.  PKV_ERR_INVALID if keep_from is outside
+ * [0, length]; PKV_ERR_STATE if the sequence is swapped out.  Forks share
+ * holes as holes; swapping a trimmed sequence moves its live blocks only
+ * (its block list carries -1 at the holes, which the swap kernels skip). */
+int pkv_seq_trim(pkv_alloc* a, int64_t seq, int64_t keep_from, int* freed_out);
 
 /* Number of blocks filed in the prefix cache. */
 int pkv_prefix_cache_size(const pkv_alloc* a, int* entries_out);

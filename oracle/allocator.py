@@ -66,6 +66,15 @@ only full blocks are shared, through reference counts):
   overwritten.
 * A plain ``append`` (or a fork inside a block) takes the sequence out of
   prefix caching for good.
+
+Sliding-window reclamation (intelliparadigm.com article, section 5.2: old
+blocks leave a sliding window and are reclaimed):
+
+* ``trim(seq, keep_from)`` releases every block wholly before position
+  keep_from, last first, as ``release`` would; its table entry becomes -1
+  (a hole) and the length does not change.
+* Holes are skipped wherever blocks are counted or released; a fork shares
+  them as holes; swapping moves live blocks only and keeps the holes.
 """
 from __future__ import annotations
 
@@ -111,7 +120,7 @@ class BlockAllocator:
         self.ref: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
-        self.swapped: Dict[int, int] = {}  # seq -> table length when swapped out
+        self.swapped: Dict[int, List[bool]] = {}  # seq -> holes of its table when swapped out
         # prefix caching
         self.cache: Dict[int, int] = {}  # block hash -> block
         self.cached_as: Dict[int, Tuple[int, Tuple[int, ...]]] = {}  # block -> (hash, token ids)
@@ -198,7 +207,8 @@ class BlockAllocator:
         nb = -(-fork_pos // self.block_size)
         shared = self.tables[parent][:nb]
         for b in shared:
-            self.ref[b] += 1
+            if b >= 0:
+                self.ref[b] += 1
         self.tables[child] = list(shared)
         self.lens[child] = fork_pos
         whole = fork_pos // self.block_size
@@ -208,10 +218,11 @@ class BlockAllocator:
         self.pending[child] = []
 
     def _give_back(self, table: List[int]) -> None:
-        for b in reversed(table):
+        live = [b for b in table if b >= 0]
+        for b in reversed(live):
             if self.ref[b] <= 0:
                 raise AllocatorError("reference count underflow")
-        for b in reversed(table):
+        for b in reversed(live):
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
@@ -234,17 +245,21 @@ class BlockAllocator:
         table = list(self.tables[seq])
         self._give_back(table)
         self.tables[seq] = []
-        self.swapped[seq] = len(table)
+        self.swapped[seq] = [b < 0 for b in table]
         return table
 
     def swap_in(self, seq: int) -> List[int]:
         if seq not in self.swapped:
             raise AllocatorError(f"sequence {seq} is not swapped out")
-        n = self.swapped[seq]
+        holes = self.swapped[seq]
+        n = sum(1 for h in holes if not h)
         if n > len(self.free):
             raise OutOfBlocks(f"need {n} blocks, {len(self.free)} free")
         table = []
-        for _ in range(n):
+        for h in holes:
+            if h:
+                table.append(-1)
+                continue
             b = self._pop()
             self.ref[b] = 1
             table.append(b)
@@ -324,6 +339,23 @@ class BlockAllocator:
         self.pending[seq] = cur
         self.lens[seq] = end
         return slots, copies, sum(1 for s in slots if s < 0)
+
+    def trim(self, seq: int, keep_from: int) -> int:
+        """Release the blocks wholly before position keep_from; returns how
+        many table entries were released."""
+        if seq not in self.tables:
+            raise AllocatorError(f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise AllocatorError(f"sequence {seq} is swapped out")
+        if not 0 <= keep_from <= self.lens[seq]:
+            raise AllocatorError("trim position outside the sequence")
+        table = self.tables[seq]
+        upto = min(keep_from // self.block_size, len(table))
+        victims = [lb for lb in range(upto) if table[lb] >= 0]
+        self._give_back([table[lb] for lb in victims])
+        for lb in victims:
+            table[lb] = -1
+        return len(victims)
 
     # -- queries ------------------------------------------------------------
     def table(self, seq: int) -> List[int]:

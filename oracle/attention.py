@@ -50,6 +50,17 @@ def gather_sequence(pool: np.ndarray, table_row, n: int, dtype: str) -> np.ndarr
     return np.concatenate(parts, axis=1)[:, :n, :]
 
 
+def gather_range(pool: np.ndarray, table_row, lo: int, n: int, dtype: str) -> np.ndarray:
+    """Tokens lo .. n-1 of a sequence, one at a time through the table
+    (token t sits in physical block table_row[t // B] at offset t % B):
+    float64 [num_kv_heads, n - lo, D].  Blocks before lo are never touched."""
+    B = pool.shape[2]
+    rows = [to_f64(pool[int(table_row[t // B]), :, t % B, :], dtype) for t in range(lo, n)]
+    if not rows:
+        return np.zeros((pool.shape[1], 0, pool.shape[3]))
+    return np.stack(rows, axis=1)
+
+
 def _softmax_weighted(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
     """softmax over the last axis of ``scores`` applied to rows of ``v``."""
     m = scores.max(axis=-1, keepdims=True)
@@ -57,9 +68,11 @@ def _softmax_weighted(scores: np.ndarray, v: np.ndarray) -> np.ndarray:
     return (e / e.sum(axis=-1, keepdims=True)) @ v
 
 
-def decode(q, k_pool, v_pool, block_tables, context_lens, scale, dtype) -> np.ndarray:
+def decode(q, k_pool, v_pool, block_tables, context_lens, scale, dtype, window: int = 0) -> np.ndarray:
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over context_lens[s]
-    tokens.  q: [S, Hq, D] raw; returns float64 [S, Hq, D]."""
+    tokens, or over the last ``window`` of them when window > 0 (a sliding
+    window: intelliparadigm.com article, section 5.2).  q: [S, Hq, D] raw;
+    returns float64 [S, Hq, D]."""
     qf = to_f64(q, dtype)
     S, Hq, D = qf.shape
     Hkv = k_pool.shape[1]
@@ -70,8 +83,13 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, dtype) -> np.nd
         n = int(context_lens[s])
         if n <= 0:
             continue
-        K = gather_sequence(k_pool, block_tables[s], n, dtype)
-        V = gather_sequence(v_pool, block_tables[s], n, dtype)
+        if window > 0:
+            lo = max(0, n - window)
+            K = gather_range(k_pool, block_tables[s], lo, n, dtype)
+            V = gather_range(v_pool, block_tables[s], lo, n, dtype)
+        else:
+            K = gather_sequence(k_pool, block_tables[s], n, dtype)
+            V = gather_sequence(v_pool, block_tables[s], n, dtype)
         for h in range(Hq):
             g = h // G
             x = sc * (K[g] @ qf[s, h])

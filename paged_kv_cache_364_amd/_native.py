@@ -58,6 +58,8 @@ SIGNATURES = {
     "pkv_decode_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "pkv_paged_attention_decode": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_float, c_int, vp, c_size, vp]),
+    "pkv_paged_attention_decode_window": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
+                                                  c_int, c_int, c_float, c_int, vp, c_size, vp]),
     "pkv_paged_attention_prefill": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp, c_int, vp, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_float, c_int, vp]),
     "pkv_alloc_create": (vp, [c_int, c_int, i32p]),
@@ -66,6 +68,7 @@ SIGNATURES = {
     "pkv_seq_append": (c_int, [vp, c_i64, c_int, i32p, i32p, c_int, intp]),
     "pkv_seq_append_tokens": (c_int, [vp, c_i64, i32p, c_int, i32p, intp, i32p, c_int, intp]),
     "pkv_prefix_cache_size": (c_int, [vp, intp]),
+    "pkv_seq_trim": (c_int, [vp, c_i64, c_i64, intp]),
     "pkv_seq_fork": (c_int, [vp, c_i64, c_i64, c_int]),
     "pkv_seq_free": (c_int, [vp, c_i64]),
     "pkv_seq_swap_out": (c_int, [vp, c_i64, i32p, c_int, intp]),

@@ -73,6 +73,13 @@ class BlockAllocator:
         N.check(st, "seq_append_tokens")
         return slots[:n], ([(int(pairs[0]), int(pairs[1]))] if nc.value else []), int(ncached.value)
 
+    def trim(self, seq: int, keep_from: int) -> int:
+        """Release the blocks wholly before position keep_from (pkv_seq_trim);
+        returns how many table entries were released."""
+        x = ctypes.c_int(0)
+        N.check(self._L.pkv_seq_trim(self._h, int(seq), int(keep_from), ctypes.byref(x)), "seq_trim")
+        return int(x.value)
+
     def prefix_cache_size(self) -> int:
         x = ctypes.c_int(0)
         N.check(self._L.pkv_prefix_cache_size(self._h, ctypes.byref(x)), "prefix_cache_size")

@@ -114,9 +114,11 @@ def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                           workspace: Optional[torch.Tensor] = None, stream=None, window: int = 0) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s through the block
-    tables (pkv_paged_attention_decode).  ``workspace`` is a uint8 GPU
+    tables (pkv_paged_attention_decode); with ``window`` > 0 only the last
+    ``window`` tokens of each context are attended
+    (pkv_paged_attention_decode_window).  ``workspace`` is a uint8 GPU
     tensor of at least decode_workspace_size(...) bytes; one is allocated
     when omitted."""
     N_, H, B, D = _cache_geometry(k_cache, v_cache)
@@ -129,11 +131,15 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(S, Hq, H, D, B, mb, q.dtype), dtype=torch.uint8,
                                 device=q.device)
-    N.check(N.lib().pkv_paged_attention_decode(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_tables, "block_tables", torch.int32), mb, _dev(context_lens, "context_lens", torch.int32), S,
-        Hq, H, D, B, N_, float(scale), _dtype_code(q), _dev(workspace, "workspace", torch.uint8),
-        workspace.numel(), _stream(stream)), "paged_attention_decode")
+    args = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), mb, _dev(context_lens, "context_lens", torch.int32), S,
+            Hq, H, D, B, N_]
+    tail = [float(scale), _dtype_code(q), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+            _stream(stream)]
+    if window and window > 0:
+        N.check(N.lib().pkv_paged_attention_decode_window(*args, int(window), *tail), "paged_attention_decode_window")
+    else:
+        N.check(N.lib().pkv_paged_attention_decode(*args, *tail), "paged_attention_decode")
     return out
 
 

@@ -49,7 +49,7 @@ struct pkv_alloc {
     std::vector<int32_t> table;
     int64_t len = 0;
     bool swapped = false;
-    int64_t swapped_blocks = 0;  // table length when it was swapped out
+    std::vector<char> swapped_holes;  // table shape when it was swapped out: 1 = hole
     // prefix caching: every append so far carried token ids
     bool tok_ok = true;
     std::vector<uint64_t> hashes;  // chained hash of each full block
@@ -347,6 +347,30 @@ int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int 
   return PKV_OK;
 }
 
+int pkv_seq_trim(pkv_alloc* a, int64_t seq, int64_t keep_from, int* freed_out) {
+  if (!a || !freed_out) return PKV_ERR_INVALID;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_ERR_INVALID;
+  pkv_alloc::Seq& s = it->second;
+  if (s.swapped) return PKV_ERR_STATE;
+  if (keep_from < 0 || keep_from > s.len) return PKV_ERR_INVALID;
+  const int64_t upto = std::min<int64_t>(keep_from / a->block_size, (int64_t)s.table.size());
+  for (int64_t lb = upto - 1; lb >= 0; --lb) {
+    const int32_t b = s.table[(size_t)lb];
+    if (b >= 0 && a->ref[(size_t)b] <= 0) return PKV_ERR_STATE;
+  }
+  int freed = 0;
+  for (int64_t lb = upto - 1; lb >= 0; --lb) {
+    const int32_t b = s.table[(size_t)lb];
+    if (b < 0) continue;
+    if (--a->ref[(size_t)b] == 0) a->free_stack.push_back(b);
+    s.table[(size_t)lb] = -1;
+    ++freed;
+  }
+  *freed_out = freed;
+  return PKV_OK;
+}
+
 int pkv_prefix_cache_size(const pkv_alloc* a, int* entries_out) {
   if (!a || !entries_out) return PKV_ERR_INVALID;
   *entries_out = (int)a->cache.size();
@@ -370,7 +394,8 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int fork_pos) {
     c.tok_ok = par.tok_ok && fork_pos % a->block_size == 0 &&
                (int64_t)par.hashes.size() >= fork_pos / a->block_size;
     if (c.tok_ok) c.hashes.assign(par.hashes.begin(), par.hashes.begin() + fork_pos / a->block_size);
-    for (int32_t b : c.table) a->ref[(size_t)b] += 1;
+    for (int32_t b : c.table)
+      if (b >= 0) a->ref[(size_t)b] += 1;  // holes (released by a trim) stay holes
     a->seqs.emplace(child, std::move(c));
   } catch (...) {
     return PKV_ERR_STATE;
@@ -384,9 +409,9 @@ int pkv_seq_free(pkv_alloc* a, int64_t seq) {
   if (it == a->seqs.end()) return PKV_ERR_INVALID;
   const std::vector<int32_t>& t = it->second.table;
   for (auto b = t.rbegin(); b != t.rend(); ++b)
-    if (a->ref[(size_t)*b] <= 0) return PKV_ERR_STATE;
+    if (*b >= 0 && a->ref[(size_t)*b] <= 0) return PKV_ERR_STATE;
   for (auto b = t.rbegin(); b != t.rend(); ++b) {
-    if (--a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
+    if (*b >= 0 && --a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
   }
   a->seqs.erase(it);
   return PKV_OK;
@@ -402,12 +427,19 @@ int pkv_seq_swap_out(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, in
   *num_out = (int)t.size();
   if ((int64_t)t.size() > cap || (!t.empty() && !blocks_out)) return PKV_ERR_INVALID;
   for (auto b = t.rbegin(); b != t.rend(); ++b)
-    if (a->ref[(size_t)*b] <= 0) return PKV_ERR_STATE;
-  for (size_t i = 0; i < t.size(); ++i) blocks_out[i] = t[i];
-  for (auto b = t.rbegin(); b != t.rend(); ++b) {
-    if (--a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
+    if (*b >= 0 && a->ref[(size_t)*b] <= 0) return PKV_ERR_STATE;
+  try {
+    s.swapped_holes.assign(t.size(), 0);
+  } catch (...) {
+    return PKV_ERR_STATE;
   }
-  s.swapped_blocks = (int64_t)t.size();
+  for (size_t i = 0; i < t.size(); ++i) {
+    blocks_out[i] = t[i];
+    s.swapped_holes[i] = t[i] < 0;
+  }
+  for (auto b = t.rbegin(); b != t.rend(); ++b) {
+    if (*b >= 0 && --a->ref[(size_t)*b] == 0) a->free_stack.push_back(*b);
+  }
   s.table.clear();
   s.swapped = true;
   return PKV_OK;
@@ -419,23 +451,28 @@ int pkv_seq_swap_in(pkv_alloc* a, int64_t seq, int32_t* blocks_out, int cap, int
   if (it == a->seqs.end()) return PKV_ERR_INVALID;
   pkv_alloc::Seq& s = it->second;
   if (!s.swapped) return PKV_ERR_STATE;
-  const int64_t n = s.swapped_blocks;
+  const int64_t n = (int64_t)s.swapped_holes.size();
   *num_out = (int)n;
   if (n > cap || (n > 0 && !blocks_out)) return PKV_ERR_INVALID;
-  if (n > (int64_t)a->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+  int64_t live = 0;
+  for (char h : s.swapped_holes) live += !h;
+  if (live > (int64_t)a->free_stack.size()) return PKV_ERR_NO_BLOCKS;
   try {
     s.table.reserve((size_t)n);
   } catch (...) {
     return PKV_ERR_STATE;
   }
   for (int64_t i = 0; i < n; ++i) {
-    const int32_t b = pop_block(a);
-    a->ref[(size_t)b] = 1;
+    int32_t b = -1;
+    if (!s.swapped_holes[(size_t)i]) {
+      b = pop_block(a);
+      a->ref[(size_t)b] = 1;
+    }
     s.table.push_back(b);
     blocks_out[i] = b;
   }
   s.swapped = false;
-  s.swapped_blocks = 0;
+  s.swapped_holes.clear();
   return PKV_OK;
 }
 
@@ -496,7 +533,7 @@ int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out) {
   int64_t toks = 0, slots = 0;
   for (const auto& kv : a->seqs) {
     toks += kv.second.len;
-    slots += (int64_t)kv.second.table.size() * a->block_size;
+    for (int32_t b : kv.second.table) slots += b >= 0 ? a->block_size : 0;
   }
   out->logical_tokens = toks;
   out->table_slots = slots;

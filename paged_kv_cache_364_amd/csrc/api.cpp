@@ -157,11 +157,10 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
   return pkv::decode_workspace_bytes(dtype, head_dim, G, num_seqs, num_kv_heads, max_blocks_per_seq, block_size);
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                               int num_blocks, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+static int decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                       int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks, int window,
+                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_kv_heads <= 0) return PKV_ERR_INVALID;
   int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                            dtype);
@@ -174,8 +173,29 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
       !aligned4(context_lens) || (workspace && !aligned16(workspace)))
     return PKV_ERR_ALIGN;
   return pkv::launch_decode(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                            num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
-                            workspace_bytes, (hipStream_t)stream);
+                            num_heads, num_kv_heads, head_dim, block_size, num_blocks, window, scale, dtype,
+                            workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, 0, scale, dtype, workspace, workspace_bytes,
+                     stream);
+}
+
+int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks, int window, float scale,
+                                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window <= 0) return PKV_ERR_INVALID;
+  return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, window, scale, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,

@@ -49,6 +49,7 @@ struct DecodeArgs {
   float* part;  // two partial slots of PSZ floats per wavefront
   int2* jobs;   // per wavefront: (unit, last wavefront) of the unit it starts, or (-1, 0)
   int S, Hq, Hkv, max_blocks, num_blocks, log2B, nW;
+  int window;   // > 0: attend only the last `window` tokens of each context
   float scale_log2;
 };
 
@@ -171,6 +172,7 @@ struct Unit {
   const char* vb;
   const int32_t* trow;
   int h, s, ctx, n, g0;  // n chunks, the first of which is global chunk g0
+  int lo, cf;            // first attended token (sliding window) and its chunk
   int nblk, wbase;
   int win0, win1;
   uint4 qv[G];
@@ -192,13 +194,15 @@ __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a,
   u.h = h;
   u.s = s;
   u.ctx = ctx;
-  u.n = (ctx + SH::NT - 1) / SH::NT;
+  u.lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+  u.cf = u.lo / SH::NT;
+  u.n = (ctx + SH::NT - 1) / SH::NT - u.cf;
   u.g0 = g0;
   u.nblk = (ctx + (1 << a.log2B) - 1) >> a.log2B;
   u.trow = a.tables + (size_t)s * a.max_blocks;
   u.kb = (const char*)a.k_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
   u.vb = (const char*)a.v_cache + (size_t)h * ((size_t)1 << a.log2B) * rowb;
-  u.wbase = (c0 * SH::NT) >> a.log2B;
+  u.wbase = ((c0 + u.cf) * SH::NT) >> a.log2B;
   u.win0 = load_window(u, u.wbase, lane);
   u.win1 = load_window(u, u.wbase + 64, lane);
   const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + (lane % SH::LR) * 16;
@@ -206,16 +210,18 @@ __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a,
   for (int g = 0; g < G; ++g) u.qv[g] = *(const uint4*)(qp + g * rowb);
 }
 
-// Issue the loads of chunk c of unit u.  Rows past the context, or whose
-// block id is out of range, are zero; the latter are flagged so that the
-// output turns into NaN instead of reading outside the pool.
+// Issue the loads of chunk c (counted from the unit's first attended chunk)
+// of unit u.  Rows outside [lo, ctx), or whose block id is out of range, are
+// zero; the latter are flagged so that the output turns into NaN instead of
+// reading outside the pool.  Table entries of blocks wholly before lo are
+// never read (a sliding window may have released them).
 template <typename T, int D, int G>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u, const DecodeArgs& a, int c,
                                            int lane) {
   using SH = DShape<T, D, G>;
   const int rg = lane / SH::LR;
   const int cl = lane % SH::LR;
-  const int t0 = c * SH::NT;
+  const int t0 = (c + u.cf) * SH::NT;
   const int B = 1 << a.log2B;
   const int lb0 = t0 >> a.log2B;
   // slide the window once the chunk has moved into its upper half; the new
@@ -243,20 +249,21 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
     const size_t ub = ((size_t)blk * blkb + (size_t)(t0 & (B - 1))) * rowb;
     const char* kp = u.kb + ub;
     const char* vp = u.vb + ub;
-    const int full = t0 + SH::NT <= u.ctx;
+    const int full = t0 >= u.lo && t0 + SH::NT <= u.ctx;
     const unsigned loff = (unsigned)(rg * D * SH::ES + cl * 16);
 #pragma unroll
     for (int j = 0; j < SH::J; ++j) {
       const int r = rg + j * SH::RW;
       const unsigned off = loff + (unsigned)(j * SH::RW * D * SH::ES);
-      if (bok && (full || t0 + r < u.ctx)) {
+      const bool in = t0 + r >= u.lo && t0 + r < u.ctx;
+      if (bok && (full || in)) {
         ch.k[j] = *(const uint4*)(kp + off);
         ch.v[j] = *(const uint4*)(vp + off);
         ch.ok |= 1 << j;
       } else {
         ch.k[j] = make_uint4(0, 0, 0, 0);
         ch.v[j] = make_uint4(0, 0, 0, 0);
-        if (t0 + r < u.ctx) ch.bad |= 1 << j;
+        if (in) ch.bad |= 1 << j;
       }
     }
   } else {
@@ -269,7 +276,7 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       const int blk = wi < 64 ? b0 : b1;
       ch.k[j] = make_uint4(0, 0, 0, 0);
       ch.v[j] = make_uint4(0, 0, 0, 0);
-      if (t < u.ctx) {
+      if (t >= u.lo && t < u.ctx) {
         if ((unsigned)blk < (unsigned)a.num_blocks) {
           const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + cl * 16;
           ch.k[j] = *(const uint4*)(u.kb + off);
@@ -424,9 +431,13 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, float* L, in
   wave_lds_sync();
 }
 
-__device__ __forceinline__ int chunks_of(int ctx, int maxctx, int nt) {
+// Chunks a unit of context ctx contributes: from the chunk of its first
+// attended token to the chunk of its last.
+__device__ __forceinline__ int chunks_of(int ctx, int maxctx, int nt, int window) {
   ctx = min(ctx, maxctx);
-  return ctx > 0 ? (ctx + nt - 1) / nt : 0;
+  if (ctx <= 0) return 0;
+  const int lo = window > 0 ? max(0, ctx - window) : 0;
+  return (ctx + nt - 1) / nt - lo / nt;
 }
 
 // Next non-empty unit after (h, s) in kv-head-major order; false at the end.
@@ -477,7 +488,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   int W1 = 0;
   for (int base = 0; base < S; base += 64) {
     const int s = base + lane;
-    W1 += wave_sum_i(s < S ? chunks_of(a.ctx_lens[s], maxctx, NT) : 0);
+    W1 += wave_sum_i(s < S ? chunks_of(a.ctx_lens[s], maxctx, NT, a.window) : 0);
   }
   const int Wtot = a.Hkv * W1;
   const int cpw = (Wtot + a.nW - 1) / max(a.nW, 1);
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   bool found = false;
   for (int base = 0; base < S; base += 64) {
     const int si = base + lane;
-    const int n = si < S ? chunks_of(a.ctx_lens[si], maxctx, NT) : 0;
+    const int n = si < S ? chunks_of(a.ctx_lens[si], maxctx, NT, a.window) : 0;
     const int incl = wave_incl_scan_i(n, lane);
     const unsigned long long hit = __ballot(P + incl > rem);
     if (hit) {
@@ -720,7 +731,7 @@ size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_b
 
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                   int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
-                  float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
   DecodeKernels k;
   if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
   const int nW = decode_waves(k, S, Hkv, max_blocks, B);
@@ -744,6 +755,7 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.log2B = 0;
   while ((1 << a.log2B) < B) ++a.log2B;
   a.nW = nW;
+  a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int grid = nW / kWavesPerWG;
   hipLaunchKernelGGL((void (*)(DecodeArgs))k.main, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);

@@ -36,7 +36,7 @@ bool decode_supported(int dtype, int head_dim, int group);
 size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_blocks, int B);
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                   int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
-                  float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int group, int block_size);
 int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,

@@ -25,7 +25,7 @@ def same_state(a: BlockAllocator, o: OracleAlloc):
     assert st.num_used == sum(1 for r in o.ref if r > 0)
     assert st.num_shared == sum(1 for r in o.ref if r > 1)
     assert st.logical_tokens == sum(o.lens.values())
-    assert st.table_slots == sum(len(t) for t in o.tables.values()) * o.block_size
+    assert st.table_slots == sum(sum(1 for b in t if b >= 0) for t in o.tables.values()) * o.block_size
     assert a.prefix_cache_size() == len(o.cache)
 
 
@@ -178,6 +178,10 @@ def test_random_prefix_cache_ops_match():
                 else:
                     s1, c1 = a.append(s, 1)
                     assert s1.tolist() == s2 and c1 == c2
+            elif r < 0.7:
+                s = live[rng.integers(len(live))]
+                keep = int(rng.integers(0, o.length(s) + 1))
+                assert a.trim(s, keep) == o.trim(s, keep)
             elif r < 0.75:
                 s = live[rng.integers(len(live))]
                 f = int(rng.integers(0, o.length(s) + 1))
@@ -210,6 +214,35 @@ def test_random_prefix_cache_ops_match():
                 o.release(s)
                 (live if s in live else swapped).remove(s)
             same_state(a, o)
+
+
+def test_trim_then_fork_swap_and_free():
+    a = BlockAllocator(16, 4)
+    o = OracleAlloc(16, 4)
+    for x in (a, o):
+        x.add(0)
+        x.append(0, 22)  # 6 blocks
+    assert a.trim(0, 9) == o.trim(0, 9) == 2  # blocks 0 and 1 wholly before position 9
+    same_state(a, o)
+    assert a.table(0)[:2] == [-1, -1]
+    assert a.trim(0, 9) == 0  # nothing left to release there
+    for x in (a, o):
+        x.fork(0, 1, 16)
+    same_state(a, o)
+    assert a.swap_out(0) == o.swap_out(0)
+    same_state(a, o)
+    assert a.swap_in(0) == o.swap_in(0)
+    same_state(a, o)
+    assert a.table(0)[:2] == [-1, -1]
+    t, lens = a.block_tables([0, 1], 6)
+    assert (t[:, :2] == -1).all() and lens.tolist() == [22, 16]
+    for x in (a, o):
+        x.release(1)
+        x.release(0)
+    same_state(a, o)
+    assert a.num_free() == 16
+    with pytest.raises(PagedKVError):
+        a.trim(5, 0)
 
 
 def test_swapped_sequence_refuses_append_and_fork():

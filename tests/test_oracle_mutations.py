@@ -214,3 +214,13 @@ def test_block_hash_over_part_of_the_block_is_caught(monkeypatch):
     real = A.block_hash
     monkeypatch.setattr(A, "block_hash", lambda prev, toks: real(0, toks[1:]))
     assert fails(P.check_prefix_cache)
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    real = attention.decode
+
+    def wider(q, k, v, t, c, scale, dtype, window=0):
+        return real(q, k, v, t, c, scale, dtype, window=window + 1 if window > 0 else 0)
+
+    monkeypatch.setattr(attention, "decode", wider)
+    assert fails(P.check_window_decode)

@@ -675,3 +675,49 @@ def check_prefix_cache_attention():
 
 def test_prefix_cache_attention():
     check_prefix_cache_attention()
+
+
+# ---------------------------------------------------------------------------
+# sliding window (intelliparadigm.com article, section 5.2)
+# ---------------------------------------------------------------------------
+def check_window_decode():
+    wl = W.decode_workload("win", 81, [1, 7, 16, 23, 40], num_heads=4, num_kv_heads=2, head_dim=8, block_size=4,
+                           num_blocks=64, dtype="f32")
+    st = runner.run(wl)
+    full = runner.expected(wl, st)
+    dec = lambda w: oracle.attention.decode(wl.q, st.k_pool, st.v_pool, st.tables, st.context_lens, wl.scale,
+                                            wl.dtype, window=w)
+    # a window at least as long as every context is the full attention
+    assert np.array_equal(dec(40), full) and np.array_equal(dec(1000), full)
+    # a one-token window returns that token's value row exactly
+    one = dec(1)
+    toks = wl.seq_tokens()
+    for i, s in enumerate(wl.batch):
+        v_last = toks[s][1][-1].view(np.float32).astype(np.float64)
+        for h in range(4):
+            assert np.array_equal(one[i, h], v_last[h // 2])
+    # brute force on the last w tokens, never paged
+    for w in (3, 5, 17):
+        o = dec(w)
+        for i, s in enumerate(wl.batch):
+            k, v = toks[s]
+            bf = oracle.attention.brute_force(wl.q[i], k[-w:], v[-w:], wl.scale, wl.dtype, group=2)
+            assert np.allclose(o[i], bf, rtol=1e-12, atol=1e-12)
+    # blocks wholly before the window may be released and reused
+    a = st.alloc
+    w = 6
+    for s in wl.batch:
+        a.trim(s, max(0, a.length(s) - w))
+    a.add(77)
+    fill, _ = a.append(77, 4 * len(a.free))
+    junk = np.full((len(fill), 2, 8), 9.0, dtype=np.float32).view(np.uint32)
+    oracle.cache.kv_write(st.k_pool, junk, fill)
+    oracle.cache.kv_write(st.v_pool, junk, fill)
+    tables, lens = a.block_tables(wl.batch, wl.max_blocks_per_seq)
+    assert (tables == -1).any()
+    after = oracle.attention.decode(wl.q, st.k_pool, st.v_pool, tables, lens, wl.scale, wl.dtype, window=w)
+    assert np.array_equal(after, dec(w))
+
+
+def test_window_decode():
+    check_window_decode()
