@@ -32,7 +32,8 @@
  *    head_dim 16, 32, 64 or 128; block_size a power of two from 1 to 256;
  *    num_heads / num_kv_heads in {1, 2, 4, 8} with head_dim * elem_bytes
  *    / 16 >= that ratio.  Prefill: bf16, head_dim 64 or 128, any of those
- *    block sizes.
+ *    block sizes, and num_blocks * num_kv_heads * block_size < 2^32 (pool
+ *    rows are indexed in 32 bits; a pool that size exceeds one GPU's HBM).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

@@ -11,7 +11,7 @@
 // Tiling.  A workgroup of eight wavefronts owns BM = 256 query rows of one
 // (sequence, head); wavefront w owns rows 32w .. 32w + 31.  Keys and values
 // are walked in tiles of KT = 64 tokens (several physical blocks gathered
-// through the table), double-buffered in LDS and staged through two sets of
+// through the table), double-buffered in LDS and staged through one set of
 // registers: the global loads of tile j + 2 are in flight while tile j is
 // computed.  The block-table entries the tiles need sit in an LDS window.
 // Per tile and wavefront:
@@ -34,6 +34,8 @@
 // only has to agree between the two operands; rows and columns follow the
 // documented 32x32 accumulator layout (lane l holds column l % 32 and rows
 // 8 * (r / 4) + 4 * (l / 32) + r % 4 of register r).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -117,11 +119,15 @@ struct KeyPiece {
 __device__ __forceinline__ KeyPiece key_piece(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t,
                                               int ctx, int D, int piece) {
   const bool in_ctx = t < ctx;
-  int blk = in_ctx ? tbl[(t >> a.log2B) - tbase] : 0;
-  const bool bad = in_ctx && (unsigned)blk >= (unsigned)a.num_blocks;
-  blk = bad ? 0 : blk;
-  const size_t row = (((size_t)blk * a.Hkv + kvh) << a.log2B) + (t & ((1 << a.log2B) - 1));
-  return {row * D + piece * 8, (in_ctx ? 0u : 1u) | (bad ? 2u : 0u)};
+  // The entry is read unconditionally (index clamped into the window) so
+  // that a tile's lookups issue together.  Past the context it may hold
+  // any value: any id inside the pool gives a valid address (the data is
+  // replaced by zeros), anything else falls back to block 0.
+  int blk = tbl[min((t >> a.log2B) - tbase, kPTableLds - 1)];
+  const bool outside = (unsigned)blk >= (unsigned)a.num_blocks;
+  blk = outside ? 0 : blk;
+  const uint32_t row = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
+  return {(size_t)row * D + piece * 8, (in_ctx ? 0u : 1u) | (in_ctx && outside ? 2u : 0u)};
 }
 
 __device__ __forceinline__ uint4 apply_fill(uint4 v, uint32_t zero, uint32_t nan, int bit) {
@@ -164,17 +170,34 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, 
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* kl, uint16_t* vl, int tid) {
   using PS = PShape<D>;
-  uint16_t* kl = buf;
-  uint16_t* vl = buf + PS::K_ELEMS;
+  uint4 kx[PS::K_LOADS], v0x[PS::V_PAIRS], v1x[PS::V_PAIRS];
+#pragma unroll
+  for (int n = 0; n < PS::K_LOADS; ++n) kx[n] = r.k[n];
+#pragma unroll
+  for (int n = 0; n < PS::V_PAIRS; ++n) {
+    v0x[n] = r.v0[n];
+    v1x[n] = r.v1[n];
+  }
+  // zero / NaN fills are needed only past the context end or for bad block
+  // ids: skipped (one scalar branch) unless some lane of the wave has one
+  if (__builtin_amdgcn_ballot_w64((r.zero | r.nan) != 0u)) {
+#pragma unroll
+    for (int n = 0; n < PS::K_LOADS; ++n) kx[n] = apply_fill(kx[n], r.zero, r.nan, n);
+#pragma unroll
+    for (int n = 0; n < PS::V_PAIRS; ++n) {
+      v0x[n] = apply_fill(v0x[n], r.zero, r.nan, PS::K_LOADS + 2 * n);
+      v1x[n] = apply_fill(v1x[n], r.zero, r.nan, PS::K_LOADS + 2 * n + 1);
+    }
+  }
 #pragma unroll
   for (int n = 0; n < PS::K_LOADS; ++n) {
     const int idx = tid + n * kPThreads;
     if (PS::K_TOTAL % kPThreads != 0 && idx >= PS::K_TOTAL) break;
     const int key = idx / PS::PIECES;
     const int pc = idx % PS::PIECES;
-    *(uint4*)(kl + key * PS::KROW + pc * 8) = apply_fill(r.k[n], r.zero, r.nan, n);
+    *(uint4*)(kl + key * PS::KROW + pc * 8) = kx[n];
   }
 #pragma unroll
   for (int n = 0; n < PS::V_PAIRS; ++n) {
@@ -183,11 +206,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
     const int pair = idx % (kPKT / 2);
     const int pc = idx / (kPKT / 2);
     const int pos = vt_pos(2 * pair);  // even; key 2 * pair + 1 sits next to it
-    const int b0 = PS::K_LOADS + 2 * n;
-    const uint4 x0 = apply_fill(r.v0[n], r.zero, r.nan, b0);
-    const uint4 x1 = apply_fill(r.v1[n], r.zero, r.nan, b0 + 1);
-    const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-    const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
+    const uint32_t a0[4] = {v0x[n].x, v0x[n].y, v0x[n].z, v0x[n].w};
+    const uint32_t a1[4] = {v1x[n].x, v1x[n].y, v1x[n].z, v1x[n].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t lo = (a0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -200,7 +220,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* buf, 
 template <int D>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * PS::BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t klds[2 * PS::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[2 * PS::V_ELEMS];
   __shared__ int tbl[kPTableLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -254,24 +275,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t sacc[2];
+  bf16x8_t pb[4];
 
   // Block-table window in LDS: entries tbase .. tbase + kPTableLds - 1 of
   // the sequence's row (those the tiles need; keys past the causal limit
   // are loaded too, then masked, so whole tiles must map to real blocks).
   const int nblk_all = (min(ctx, n_tiles * kPKT) + (1 << a.log2B) - 1) >> a.log2B;
   int tbase = 0;
-  auto fill_window = [&](int base) {
+  auto fill_window = [&](int base) __attribute__((always_inline)) {
     const int n = min(nblk_all - base, kPTableLds);
     for (int i = tid; i < n; i += kPThreads) tbl[i] = trow[base + i];
   };
   fill_window(0);
   __syncthreads();
 
-  // Key tiles flow global -> registers -> LDS.  Two register stages: while
-  // tile j is computed from LDS buffer j % 2, tile j + 1 (loaded one
-  // iteration earlier) waits in one stage and tile j + 2 loads into the
-  // other, so a tile's loads have a whole iteration to arrive.
-  auto load = [&](TileRegs<D>& r, int jt) {
+  auto load = [&](TileRegs<D>& r, int jt) __attribute__((always_inline)) {
     // slide the window when tile jt leaves it (uniform over the workgroup)
     const int last_blk = (min((jt + 1) * kPKT, ctx) - 1) >> a.log2B;
     if (last_blk >= tbase + kPTableLds) {
@@ -282,96 +301,63 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
     load_tile<D>(r, a, tbl, tbase, kvh, jt * kPKT, ctx, tid);
   };
-  auto compute = [&](int j) {
-    const uint16_t* buf = lds + (j & 1) * PS::BUF_ELEMS;
-    const int t0 = j * kPKT;
-    if (wave_live && t0 <= wave_last_pos) {
-      const uint16_t* kl = buf;
-      const uint16_t* vl = buf + PS::K_ELEMS;
-      // S^T for keys t0 .. t0 + 63 (two 32-key tiles) x this wave's 32
-      // queries.  The two accumulators alternate and the K fragments of
-      // the next contraction step are read while this step's products run.
-      f32x16_t sacc[2];
+  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && j * kPKT <= wave_last_pos; };
+
+  // S^T for keys 64j .. 64j + 63 (two 32-key tiles) x this wave's 32
+  // queries.  The two accumulators alternate; the K fragments are read two
+  // contraction steps ahead, in an order the scheduler may not sink.
+  auto s_phase = [&](int j) __attribute__((always_inline)) {
+    const uint16_t* k0 = klds + (j & 1) * PS::K_ELEMS + lq * PS::KROW + hh * 8;
+    const uint16_t* k1 = k0 + 32 * PS::KROW;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+    uint4 f0[PS::KS], f1[PS::KS];
+    f0[0] = *(const uint4*)k0;
+    f1[0] = *(const uint4*)k1;
+    f0[1] = *(const uint4*)(k0 + 16);
+    f1[1] = *(const uint4*)(k1 + 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < PS::KS; ++ks) {
+      if (ks + 2 < PS::KS) {
+        f0[ks + 2] = *(const uint4*)(k0 + (ks + 2) * 16);
+        f1[ks + 2] = *(const uint4*)(k1 + (ks + 2) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[ks]), qreg[ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1[ks]), qreg[ks], sacc[1], 0, 0, 0);
+    }
+  };
+
+  // Online softmax of tile j: weights P^T = exp2(c * s - m) in bf16 (c =
+  // scale * log2 e), grouped by 16-key contraction steps, and the row sum
+  // of those bf16 weights (v_dot2 with ones, so it adds what the matrix
+  // cores see).  The reference m of a row is not moved every tile: weights
+  // are formed against the current m, and only when a lane's weights sum
+  // past 2^8 (a score above m by more than 8 in the log2 domain), or the
+  // row has no reference yet, is the tile's true maximum taken, m raised
+  // to it, the accumulators rescaled and the weights formed again.  So
+  // weights stay below 2^8 (bf16 and fp32 hold them exactly as scaled
+  // values), and the final division by the row sum, taken against the same
+  // references, cancels m exactly.  Masked keys (causal limit) occur only
+  // in the tiles on the wave's diagonal, which take the masked variant.
+  const float c = a.scale_log2;
+  auto softmax = [&](auto masked, int t0) __attribute__((always_inline)) {
+    constexpr bool M = decltype(masked)::value;
+    if constexpr (M) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-      {
-        const uint16_t* k0 = kl + lq * PS::KROW + hh * 8;
-        const uint16_t* k1 = k0 + 32 * PS::KROW;
-        uint4 fa0 = *(const uint4*)k0, fa1 = *(const uint4*)k1;
-#pragma unroll
-        for (int ks = 0; ks < PS::KS; ++ks) {
-          uint4 fb0, fb1;
-          if (ks + 1 < PS::KS) {
-            fb0 = *(const uint4*)(k0 + (ks + 1) * 16);
-            fb1 = *(const uint4*)(k1 + (ks + 1) * 16);
-          }
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa0), qreg[ks], sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa1), qreg[ks], sacc[1], 0, 0, 0);
-          if (ks + 1 < PS::KS) {
-            fa0 = fb0;
-            fa1 = fb1;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int t = t0 + mt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          sacc[mt][r] = t > my_pos ? -INFINITY : sacc[mt][r] * c;
         }
-      }
-      // Scores in the log2 domain are c * s (c = scale * log2 e).  The tile
-      // max of a row is taken on the raw scores (c * max s, or c * min s
-      // for c < 0); masked keys (causal limit, context end) only occur in
-      // tiles on the diagonal or at the end, which take the select path.
-      const float c = a.scale_log2;
-      const bool need_mask = (t0 + kPKT - 1 > P + wr0) || (t0 + kPKT > ctx);
-      float tmax;
-      if (need_mask) {
-        tmax = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int t = t0 + mt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float x = (t > my_pos || t >= ctx) ? -INFINITY : sacc[mt][r] * c;
-            sacc[mt][r] = x;
-            tmax = fmaxf(tmax, x);
-          }
-      } else {
-        float hi = sacc[0][0], lo = sacc[0][0];
-        if (c >= 0.f) {
-#pragma unroll
-          for (int i = 1; i < 31; i += 2)
-            hi = __builtin_fmaxf(hi, __builtin_fmaxf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
-          hi = fmaxf(hi, sacc[1][15]);
-          tmax = c * hi;
-        } else {
-#pragma unroll
-          for (int i = 1; i < 31; i += 2)
-            lo = __builtin_fminf(lo, __builtin_fminf(sacc[i >> 4][i & 15], sacc[(i + 1) >> 4][(i + 1) & 15]));
-          lo = fminf(lo, sacc[1][15]);
-          tmax = c * lo;
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      // Lazy running max: the reference m_run moves only when a score
-      // exceeds it by more than 2^8 (or on the first live tile), so the
-      // accumulators are rescaled rarely; weights stay below 256, well
-      // inside bf16 and fp32 range, and the final division by the row sum
-      // taken against the same reference cancels it exactly.
-      const bool move = tmax > m_run + 8.f;  // false while the row is all masked (tmax = -inf)
-      const float m_new = move ? tmax : m_run;
-      if (__ballot(move)) {
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // exp2(-inf) = 0 at the start
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < PS::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      }
-      m_run = m_new;
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;  // masked rows so far: weights 0
-      // P^T in bf16, grouped by 16-key contraction steps; the row sum adds
-      // the bf16 weights the matrix cores see (v_dot2 with ones)
-      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+    }
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+    auto weights = [&](float msub) __attribute__((always_inline)) {
       float psum = 0.f;
-      bf16x8_t pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint32_t w4[4];
@@ -379,57 +365,105 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 8; e += 2) {
           const float x0 = sacc[kk >> 1][8 * (kk & 1) + e];
           const float x1 = sacc[kk >> 1][8 * (kk & 1) + e + 1];
-          const float p0 = __builtin_amdgcn_exp2f(need_mask ? x0 - msub : __builtin_fmaf(x0, c, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(need_mask ? x1 - msub : __builtin_fmaf(x1, c, -msub));
+          const float p0 = __builtin_amdgcn_exp2f(M ? x0 - msub : __builtin_fmaf(x0, c, -msub));
+          const float p1 = __builtin_amdgcn_exp2f(M ? x1 - msub : __builtin_fmaf(x1, c, -msub));
           w4[e >> 1] = pack2_bf16(p0, p1);
           psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[e >> 1]), ones, psum, false);
         }
         pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
-      l_run += psum;
-      // O^T += V^T P^T: the DT accumulators alternate; the V^T fragments
-      // of the next contraction step are read while this step's run
-      {
-        const uint16_t* v0 = vl + lq * PS::VROW + hh * 8;
-        uint4 fa[PS::DT], fb[PS::DT];
+      return psum;
+    };
+    bool slow = m_run == -INFINITY;
+    float psum = 0.f;
+    if (!__builtin_amdgcn_ballot_w64(slow)) {
+      psum = weights(m_run);
+      slow = psum > 256.f;  // false for NaN: such rows stay NaN
+    }
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+      float tmax;
+      if constexpr (M) {
+        tmax = sacc[0][0];
 #pragma unroll
-        for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW);
+        for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, sacc[i >> 4][i & 15]);
+      } else {
+        float hi = sacc[0][0], lo = sacc[0][0];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          if (kk + 1 < 4) {
-#pragma unroll
-            for (int dt = 0; dt < PS::DT; ++dt) fb[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW + (kk + 1) * 16);
-          }
-#pragma unroll
-          for (int dt = 0; dt < PS::DT; ++dt)
-            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[dt]), pb[kk], acc_o[dt], 0, 0, 0);
-          if (kk + 1 < 4) {
-#pragma unroll
-            for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = fb[dt];
-          }
+        for (int i = 1; i < 32; ++i) {
+          hi = fmaxf(hi, sacc[i >> 4][i & 15]);
+          lo = fminf(lo, sacc[i >> 4][i & 15]);
         }
+        tmax = c * (c >= 0.f ? hi : lo);
       }
-        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);  // stays -inf while the row is all masked
+      const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // exp2(-inf) = 0
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      m_run = m_new;
+      psum = weights(m_run == -INFINITY ? 0.f : m_run);
+    }
+    l_run += psum;
   };
-  // one iteration: tile j + 1 waits in `ready`, `spare` receives tile j + 2
-  auto iteration = [&](int j, TileRegs<D>& ready, TileRegs<D>& spare) {
-    // issued every iteration (the last tile again near the end, unused) so
-    // that the wait for `ready` below never has to cover these loads
-    load(spare, min(j + 2, n_tiles - 1));
-    compute(j);
-    if (j + 1 < n_tiles) store_tile<D>(ready, lds + ((j + 1) & 1) * PS::BUF_ELEMS, tid);
+  auto sm_phase = [&](int j) __attribute__((always_inline)) {
+    const int t0 = j * kPKT;
+    if (t0 + kPKT - 1 > P + wr0)
+      softmax(std::true_type{}, t0);
+    else
+      softmax(std::false_type{}, t0);
+  };
+
+  // O^T += V^T P^T: the DT accumulators alternate; the V^T fragments of the
+  // next contraction step are read while this step's products run
+  auto o_phase = [&](int j) __attribute__((always_inline)) {
+    const uint16_t* v0 = vlds + (j & 1) * PS::V_ELEMS + lq * PS::VROW + hh * 8;
+    uint4 fa[PS::DT], fb[PS::DT];
+#pragma unroll
+    for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < PS::DT; ++dt) fb[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW + (kk + 1) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < PS::DT; ++dt)
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[dt]), pb[kk], acc_o[dt], 0, 0, 0);
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = fb[dt];
+      }
+    }
+  };
+
+  // Key tiles flow global -> registers -> LDS through one register stage,
+  // double buffered in LDS: step j first writes tile j + 1 (loaded during
+  // step j - 1) over tile j - 1, then issues the loads of tile j + 2 into the
+  // same registers, then computes tile j, so a tile's loads have a whole
+  // step of compute to arrive.
+  TileRegs<D> rg;
+  auto step = [&](int j) __attribute__((always_inline)) {
+    if (j + 1 < n_tiles) {
+      store_tile<D>(rg, klds + ((j + 1) & 1) * PS::K_ELEMS, vlds + ((j + 1) & 1) * PS::V_ELEMS, tid);
+      if (j + 2 < n_tiles) load(rg, j + 2);
+    }
+    if (live(j)) {
+      s_phase(j);
+      sm_phase(j);
+      o_phase(j);
+    }
     __syncthreads();
   };
 
-  TileRegs<D> ra, rb;
-  load(ra, 0);
-  load(rb, min(1, n_tiles - 1));
-  store_tile<D>(ra, lds, tid);
+  load(rg, 0);
+  store_tile<D>(rg, klds, vlds, tid);
+  if (n_tiles > 1) load(rg, 1);
   __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
-    iteration(j, rb, ra);
-    if (j + 1 < n_tiles) iteration(j + 1, ra, rb);
-  }
+  for (int j = 0; j < n_tiles; ++j) step(j);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
