@@ -36,6 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
 # HBM bytes per dispatch from rocprofv3 counters (written by
 # paged_kv_cache_364_amd.profiling from two --pmc runs of this script)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama31_8b_b64_prefill_opt13b_b16x512.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util_prefill_opt13b_b16x512.txt")
 
 
 def log(msg):
@@ -123,17 +124,23 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
     log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
         f"{kw_ms * 1e3:.1f} us")
     traffic = None
+    mfma = {"mfma_util_pct": None, "executed_gflop": None}
     try:
         from paged_kv_cache_364_amd import profiling
 
         tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE), ["prefill_kernel<128>"])
         traffic = round(tb / 1e9, 4) if tb is not None else None
+        # matrix-core counters of the same kernel, if taken from these sources
+        e = profiling.read_traffic(MFMA_FILE).get("kernels", {}).get("prefill_kernel<128>")
+        if e is not None and e.get("sources_sha256") == profiling.sources_sha(e["group"]):
+            mfma = {"mfma_util_pct": round(e["mfma_util_pct"], 2), "executed_gflop": round(e["bf16_flops"] / 1e9, 3)}
     except Exception:
         traffic = None
     res = {
         "workload": wl.name, "num_seqs": S, "chunk": int(C[0]), "prefix_lens": "uniform 0..1536 (seed 5)",
         "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": B, "layers_rotated": L,
         "prefill_us_avg": round(pf_ms * 1e3, 2),
+        "prefill_us_median": round(float(np.median(pf_all)) * 1e3, 2),
         "prefill_us_p10": round(float(np.percentile(pf_all, 10)) * 1e3, 2),
         "prefill_us_p90": round(float(np.percentile(pf_all, 90)) * 1e3, 2),
         "kv_write_chunk_us_avg": round(kw_ms * 1e3, 2),
@@ -143,6 +150,7 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128>", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "rocprof_mfma": mfma,
     }
     del kps, vps
     return res, (wl, st, out)
@@ -431,6 +439,7 @@ def main():
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_us_avg": round(dec_avg * 1e3, 2),
+        "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
         "decode_only_us_avg": round(dec_only_ms * 1e3, 2),

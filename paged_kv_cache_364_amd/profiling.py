@@ -12,6 +12,12 @@
     library, plus a JSON line that ``bench.py`` reads back.  The JSON carries
     the SHA-256 of the kernel sources, so a figure taken before a kernel
     changed is not reported for the new one.
+
+``python -m paged_kv_cache_364_amd.profiling mfma DIR OUT.txt CMD...``
+    reads a ``--pmc MfmaUtil MfmaFlopsBF16`` run (rocprofv3's derived
+    counters: matrix-core busy cycles over active cycles of all SIMDs, and
+    bf16 matrix flops executed) and writes their per-dispatch medians for
+    every kernel of this library, plus a JSON line like the traffic one.
 """
 from __future__ import annotations
 
@@ -118,6 +124,37 @@ def traffic_summary(fetch_dir: str, write_dir: str, cal_bytes: int, out: str, cm
     return result
 
 
+def mfma_summary(d: str, out: str, cmd: str) -> Dict:
+    util, flops = _pmc(d, "MfmaUtil"), _pmc(d, "MfmaFlopsBF16")
+    per: Dict[str, Dict[str, List[float]]] = {}
+    for rows, key in ((util, "util"), (flops, "flops")):
+        for r in rows:
+            g = kernel_group(r["Kernel_Name"])
+            if not g:
+                continue
+            e = per.setdefault(short(r["Kernel_Name"]), {"util": [], "flops": [], "ns": []})
+            e[key].append(float(r["Counter_Value"]))
+            if key == "util":
+                e["ns"].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    result: Dict = {"kernels": {}}
+    lines = ["# Matrix-core use per dispatch (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16)", f"command: {cmd}", "",
+             "MfmaUtil = matrix-core busy cycles summed over SIMDs / (active cycles x SIMDs), percent;",
+             "MfmaFlopsBF16 = bf16 matrix flops executed (masked and padded work included).", "",
+             f"{'kernel':40s} {'n':>3s} {'MfmaUtil %':>11s} {'GFLOP exec':>11s} {'us (pmc run)':>13s}"]
+    for name, v in per.items():
+        if not v["util"] or not v["flops"]:
+            continue
+        u, fl, ns = statistics.median(v["util"]), statistics.median(v["flops"]), statistics.median(v["ns"])
+        g = kernel_group(name)
+        result["kernels"][name] = {"mfma_util_pct": u, "bf16_flops": fl, "group": g,
+                                   "sources_sha256": sources_sha(g)}
+        lines.append(f"{name[:40]:40s} {len(v['util']):3d} {u:11.2f} {fl / 1e9:11.2f} {ns / 1e3:13.1f}")
+    lines += ["", "json: " + json.dumps(result, sort_keys=True)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return result
+
+
 def read_traffic(path: str) -> Dict:
     """The JSON line of a traffic summary, or {} when absent."""
     if not os.path.exists(path):
@@ -147,5 +184,7 @@ if __name__ == "__main__":
     elif mode == "traffic":
         print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5],
                                          " ".join(sys.argv[6:])), indent=1))
+    elif mode == "mfma":
+        print(json.dumps(mfma_summary(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:])), indent=1))
     else:
         raise SystemExit(__doc__)
