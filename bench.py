@@ -253,6 +253,63 @@ def window_leg(torch, np, api, driver, workloads, dev, steps, warmup, window=512
     return res
 
 
+def unique_kv_tokens(np, tables, lens, B):
+    """Tokens held by distinct physical blocks: a block shared by several
+    tables counts once, with the most positions any of them uses."""
+    held = {}
+    for t, n in zip(tables, lens):
+        for lb in range((int(n) + B - 1) // B):
+            b = int(t[lb])
+            held[b] = max(held.get(b, 0), min(B, int(n) - lb * B))
+    return sum(held.values())
+
+
+def config_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4):
+    """Decode on the other Llama-3.1-8B-shape batches: 256 log-normal
+    contexts over a churned free list, and 32 prompts forked into 4 branches
+    that share their prompt blocks.  Each rotates `layers` copies of its
+    pools so that the working set exceeds the Infinity Cache."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    for build, desc in ((workloads.config3, "256 contexts, log-normal (median 500, sigma 1, clip 1..8192), "
+                                            "churned free list (seed 3)"),
+                        (workloads.config4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023}, "
+                                            "U{0..256} private tokens each (seed 4)")):
+        wl = build()
+        st = driver.run_script(wl, device=dev)
+        torch.cuda.synchronize()
+        S, Hq, Hkv, D, B = len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+        lens = st.context_lens.astype(np.int64)
+        kv_bytes = int(lens.sum()) * Hkv * D * 2 * 2
+        uniq_bytes = unique_kv_tokens(np, st.tables, lens, B) * Hkv * D * 2 * 2
+        kps, vps = [st.k_pool], [st.v_pool]
+        for _ in range(1, layers):
+            kps.append(st.k_pool.clone())
+            vps.append(st.v_pool.clone())
+        q = driver.to_device(wl.q, wl.dtype, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+                         dtype=torch.uint8, device=dev)
+
+        def decode(i):
+            api.paged_attention_decode(out, q, kps[i % layers], vps[i % layers], st.tables_dev, st.lens_dev,
+                                       float(wl.scale), workspace=ws)
+
+        ms, all_ms = timed_calls(torch, decode, steps, warmup, stream)
+        med = float(np.median(all_ms))
+        r = {"workload": wl.name, "batch": desc, "num_seqs": S, "sum_context": int(lens.sum()),
+             "layers_rotated": layers, "decode_us_avg": round(ms * 1e3, 2), "decode_us_median": round(med * 1e3, 2),
+             "kv_bytes_logical": kv_bytes, "kv_gbps_logical": round(kv_bytes / (med * 1e-3) / 1e9, 1),
+             "kv_bytes_unique": uniq_bytes, "kv_gbps_unique": round(uniq_bytes / (med * 1e-3) / 1e9, 1),
+             "pct_hbm_peak_unique": round(100 * uniq_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+             "seqs_per_s_per_layer": round(S / (med * 1e-3), 1)}
+        log(f"{wl.name}: {r}")
+        res[wl.name] = r
+        del st, kps, vps, q, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def block_sweep(args, torch, np, api, driver, workloads, dev):
     """Decode at the Llama-3.1-8B shape for several block sizes with the same
     lengths and values (seed 2) and the same pool capacity (409,600 tokens
@@ -307,6 +364,7 @@ def main():
     ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--no-prefix-cache", action="store_true")
     ap.add_argument("--no-window", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the ragged and shared-prefix decode batches")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
@@ -465,6 +523,8 @@ def main():
         result["sliding_window"] = window_leg(torch, np, api, driver, workloads, dev, 50, 5)
     if not args.no_prefix_cache:
         result["prefix_cache"] = prefix_cache_leg(torch, np, api, driver, workloads, dev, 50, 5)
+    if not args.no_configs:
+        result["other_batches"] = config_legs(torch, np, api, driver, workloads, dev, 50, 5)
 
     pf = None
     if not args.no_prefill:
