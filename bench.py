@@ -43,20 +43,33 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def timed_calls(torch, fn, n, warmup, stream):
-    """Average time per call (ms) of ``fn(i)`` from events recorded on the
-    stream the kernels run on, plus the list of per-call times."""
+def timed_calls(torch, fn, n, warmup, stream, per_call=True):
+    """Average time per call (ms) of ``fn(i)``: one pair of events, recorded
+    on the stream the kernels run on, around n calls back to back (an event
+    recorded between two kernels adds a gap of its own, several microseconds
+    here, to every call it brackets).  With ``per_call``, a second pass with
+    an event pair around each call gives the per-call times, for their
+    spread only."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(n):
-        evs[i][0].record(stream)
         fn(warmup + i)
-        evs[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ts = [a.elapsed_time(b) for a, b in evs]
-    return sum(ts) / len(ts), ts
+    avg = e0.elapsed_time(e1) / n
+    ts = []
+    if per_call:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            fn(warmup + n + i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+    return avg, ts
 
 
 def copy_bandwidth(torch, api, dev, mib=2048):
@@ -123,15 +136,17 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
     tflops = flops / (pf_ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
         f"{kw_ms * 1e3:.1f} us")
+    # the instantiation this shape runs (blocks of two or more tokens pair V rows)
+    kname = f"prefill_kernel<{D}, {'true' if B >= 2 else 'false'}>"
     traffic = None
     mfma = {"mfma_util_pct": None, "executed_gflop": None}
     try:
         from paged_kv_cache_364_amd import profiling
 
-        tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE), ["prefill_kernel<128>"])
+        tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE), [kname])
         traffic = round(tb / 1e9, 4) if tb is not None else None
         # matrix-core counters of the same kernel, if taken from these sources
-        e = profiling.read_traffic(MFMA_FILE).get("kernels", {}).get("prefill_kernel<128>")
+        e = profiling.read_traffic(MFMA_FILE).get("kernels", {}).get(kname)
         if e is not None and e.get("sources_sha256") == profiling.sources_sha(e["group"]):
             mfma = {"mfma_util_pct": round(e["mfma_util_pct"], 2), "executed_gflop": round(e["bf16_flops"] / 1e9, 3)}
     except Exception:
@@ -140,14 +155,14 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         "workload": wl.name, "num_seqs": S, "chunk": int(C[0]), "prefix_lens": "uniform 0..1536 (seed 5)",
         "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": B, "layers_rotated": L,
         "prefill_us_avg": round(pf_ms * 1e3, 2),
-        "prefill_us_median": round(float(np.median(pf_all)) * 1e3, 2),
-        "prefill_us_p10": round(float(np.percentile(pf_all, 10)) * 1e3, 2),
-        "prefill_us_p90": round(float(np.percentile(pf_all, 90)) * 1e3, 2),
+        "prefill_us_per_call_events": {"median": round(float(np.median(pf_all)) * 1e3, 2),
+                                       "p10": round(float(np.percentile(pf_all, 10)) * 1e3, 2),
+                                       "p90": round(float(np.percentile(pf_all, 90)) * 1e3, 2)},
         "kv_write_chunk_us_avg": round(kw_ms * 1e3, 2),
         "tflops": round(tflops, 2), "algorithmic_gflop": round(flops / 1e9, 3),
         "min_hbm_bytes": kv_bytes + qo_bytes,
         "hbm_gbps_at_min_bytes": round((kv_bytes + qo_bytes) / (pf_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128>", "achieved": round(tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "rocprof_mfma": mfma,
@@ -296,13 +311,13 @@ def config_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4)
                                        float(wl.scale), workspace=ws)
 
         ms, all_ms = timed_calls(torch, decode, steps, warmup, stream)
-        med = float(np.median(all_ms))
         r = {"workload": wl.name, "batch": desc, "num_seqs": S, "sum_context": int(lens.sum()),
-             "layers_rotated": layers, "decode_us_avg": round(ms * 1e3, 2), "decode_us_median": round(med * 1e3, 2),
-             "kv_bytes_logical": kv_bytes, "kv_gbps_logical": round(kv_bytes / (med * 1e-3) / 1e9, 1),
-             "kv_bytes_unique": uniq_bytes, "kv_gbps_unique": round(uniq_bytes / (med * 1e-3) / 1e9, 1),
-             "pct_hbm_peak_unique": round(100 * uniq_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-             "seqs_per_s_per_layer": round(S / (med * 1e-3), 1)}
+             "layers_rotated": layers, "decode_us_avg": round(ms * 1e3, 2),
+             "decode_us_per_call_events_median": round(float(np.median(all_ms)) * 1e3, 2),
+             "kv_bytes_logical": kv_bytes, "kv_gbps_logical": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+             "kv_bytes_unique": uniq_bytes, "kv_gbps_unique": round(uniq_bytes / (ms * 1e-3) / 1e9, 1),
+             "pct_hbm_peak_unique": round(100 * uniq_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+             "seqs_per_s_per_layer": round(S / (ms * 1e-3), 1)}
         log(f"{wl.name}: {r}")
         res[wl.name] = r
         del st, kps, vps, q, out, ws
@@ -437,39 +452,35 @@ def main():
         li = i % L
         api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
 
-    def step(i, ev=None):
+    def write(i):
         li = i % L
-        if ev is not None:
-            ev[0].record(stream)
         api.kv_write(kn, vn, slots, kps[li], vps[li])
-        if ev is not None:
-            ev[1].record(stream)
-        api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(i):
+        write(i)
+        decode(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    # timed region: K whole steps, wall clock between two synchronisations;
-    # per-kernel events ride along on the kernels' stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # timed region: K whole steps back to back, wall clock between two
+    # synchronisations, nothing else enqueued inside it
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    kvw_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_per_step = t_total * 1e3 / K
-    dec_avg = float(dec_ms.mean())
-    log(f"decode avg {dec_avg * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); kv_write avg {kvw_ms.mean() * 1e3:.1f} us; "
-        f"wall {ms_per_step * 1e3:.1f} us/step")
-    # decode alone, back to back (no kv_write between calls)
-    dec_only_ms, _ = timed_calls(torch, decode, K, 5, stream)
+    # per-call durations: K decode calls (then K kv_write calls) back to back
+    # between one pair of events on the kernels' stream
+    dec_avg, dec_ms = timed_calls(torch, decode, K, 5, stream)
+    dec_ms = np.array(dec_ms)
+    kvw_avg, _ = timed_calls(torch, write, K, 5, stream, per_call=False)
+    log(f"decode avg {dec_avg * 1e3:.1f} us (per-call events: median {np.median(dec_ms) * 1e3:.1f}, "
+        f"p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
+        f"kv_write avg {kvw_avg * 1e3:.1f} us; wall {ms_per_step * 1e3:.1f} us/step")
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = (kv_bytes + qo_bytes) / (dec_avg * 1e-3) / 1e9
@@ -497,11 +508,14 @@ def main():
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_us_avg": round(dec_avg * 1e3, 2),
-        "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
-        "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-        "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-        "decode_only_us_avg": round(dec_only_ms * 1e3, 2),
-        "kv_write_us_avg": round(float(kvw_ms.mean()) * 1e3, 2),
+        "decode_us_per_call_events": {"median": round(float(np.median(dec_ms)) * 1e3, 2),
+                                      "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                                      "note": "an event pair around each call; each event adds its own gap"},
+        "kv_write_us_avg": round(kvw_avg * 1e3, 2),
+        "kv_write_us_in_step": round((ms_per_step - dec_avg) * 1e3, 2),
+        "kv_write_note": "alone, back to back, the 64-token write is bound by the host's launch rate; "
+                         "kv_write_us_in_step = wall per step - decode average",
         "roofline": {"bound": "hbm", "kernel": "paged_attention_decode = decode_main + decode_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -136,7 +136,7 @@ __device__ __forceinline__ uint4 apply_fill(uint4 v, uint32_t zero, uint32_t nan
   return v;
 }
 
-template <int D>
+template <int D, bool PAIRED>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int* tbl, int tbase, int kvh,
                                           int t0, int ctx, int tid) {
   using PS = PShape<D>;
@@ -161,7 +161,15 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, 
     const int pc = idx / (kPKT / 2);
     const int b0 = PS::K_LOADS + 2 * n;
     const KeyPiece p0 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair, ctx, D, pc);
-    const KeyPiece p1 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx, D, pc);
+    KeyPiece p1;
+    if constexpr (PAIRED) {
+      // blocks of two or more tokens: keys 2 * pair and 2 * pair + 1 share
+      // a block, so the second row follows the first
+      const bool in1 = t0 + 2 * pair + 1 < ctx;
+      p1 = {p0.off + D, (in1 ? 0u : 1u) | (in1 && (p0.code & 3u) == 2u ? 2u : 0u)};
+    } else {
+      p1 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx, D, pc);
+    }
     r.v0[n] = *(const uint4*)(a.v_cache + p0.off);
     r.v1[n] = *(const uint4*)(a.v_cache + p1.off);
     r.zero |= ((p0.code & 1u) << b0) | ((p1.code & 1u) << (b0 + 1));
@@ -208,16 +216,16 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* kl, u
     const int pos = vt_pos(2 * pair);  // even; key 2 * pair + 1 sits next to it
     const uint32_t a0[4] = {v0x[n].x, v0x[n].y, v0x[n].z, v0x[n].w};
     const uint32_t a1[4] = {v1x[n].x, v1x[n].y, v1x[n].z, v1x[n].w};
+    // element e of key 2 * pair (low half) and of key 2 * pair + 1 (high
+    // half) in one v_perm_b32: byte selectors 0-3 pick from a0, 4-7 from a1
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (a0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      const uint32_t hi = (a1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      *(uint32_t*)(vl + (pc * 8 + e) * PS::VROW + pos) = lo | (hi << 16);
-    }
+    for (int e = 0; e < 8; ++e)
+      *(uint32_t*)(vl + (pc * 8 + e) * PS::VROW + pos) =
+          __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
   }
 }
 
-template <int D>
+template <int D, bool PAIRED>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
   __shared__ __attribute__((aligned(16))) uint16_t klds[2 * PS::K_ELEMS];
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       fill_window(tbase);
       __syncthreads();
     }
-    load_tile<D>(r, a, tbl, tbase, kvh, jt * kPKT, ctx, tid);
+    load_tile<D, PAIRED>(r, a, tbl, tbase, kvh, jt * kPKT, ctx, tid);
   };
   auto live = [&](int j) __attribute__((always_inline)) { return wave_live && j * kPKT <= wave_last_pos; };
 
@@ -513,10 +521,15 @@ int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total
   const long long grid = (units + 7) / 8 * 8 * a.q_tiles;
   if (grid <= 0) return 0;
   if (grid > 0x7fffffffLL) return -2;
-  if (D == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, a);
+  const dim3 g((unsigned)grid), b(kPThreads);
+  if (D == 128 && B >= 2)
+    hipLaunchKernelGGL((prefill_kernel<128, true>), g, b, 0, stream, a);
+  else if (D == 128)
+    hipLaunchKernelGGL((prefill_kernel<128, false>), g, b, 0, stream, a);
+  else if (D == 64 && B >= 2)
+    hipLaunchKernelGGL((prefill_kernel<64, true>), g, b, 0, stream, a);
   else if (D == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(kPThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<64, false>), g, b, 0, stream, a);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -6;
