@@ -96,3 +96,14 @@ def test_prefill_rejects_bad_arguments():
         == N.PKV_ERR_UNSUPPORTED
     assert L.pkv_paged_attention_prefill(p, p, p, -1, 10, p, p, p, 4, p, 2, 8, 8, 128, 16, 64, 0.1, 1, None) \
         == N.PKV_ERR_INVALID
+    # nothing to do: no launch, whatever the pointers
+    assert L.pkv_paged_attention_prefill(p, p, p, 0, 0, p, p, p, 4, p, 2, 8, 8, 128, 16, 64, 0.1, 1, None) \
+        == N.PKV_OK
+    # fp32 has no matrix-core path
+    assert L.pkv_paged_attention_prefill(p, p, p, 10, 10, p, p, p, 4, p, 2, 8, 8, 128, 16, 64, 0.1, 0, None) \
+        == N.PKV_ERR_UNSUPPORTED
+    # pool rows (block, kv head, slot) are indexed in 32 bits
+    assert L.pkv_paged_attention_prefill(p, p, p, 10, 10, p, p, p, 4, p, 2, 8, 8, 128, 16, 1 << 25, 0.1, 1,
+                                         None) == N.PKV_ERR_UNSUPPORTED
+    assert L.pkv_paged_attention_prefill(p, p, p, 0, 0, p, p, p, 4, p, 2, 8, 8, 128, 16, (1 << 25) - 1, 0.1, 1,
+                                         None) == N.PKV_OK

@@ -69,6 +69,12 @@ def test_prefill_variants(hq, hkv, d, b):
     check(small(f"pf-{hq}-{hkv}-{d}-{b}", 60 + hq + d + b, [0, 5, 100, 63], [17, 64, 77, 129], hq, hkv, d, b))
 
 
+def test_prefill_empty_chunks_and_single_token():
+    """Chunks of zero rows, with and without a cached prefix, between others,
+    and a sequence whose whole context is its chunk's single row."""
+    check(small("pf-empty", 77, [10, 0, 40, 0, 7], [5, 0, 33, 1, 0], 4, 2, 64, 16))
+
+
 def test_prefill_table_window_slides():
     """Block size 1 and contexts past 1024 blocks: the workgroup's LDS window
     of the block table has to slide while the key tiles advance."""
