@@ -43,6 +43,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_description(np):
+    """CPU model, usable cores and the numpy / BLAS builds the oracle ran on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()}))
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "sched_affinity": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas}
+
+
 def timed_calls(torch, fn, n, warmup, stream, per_call=True):
     """Average time per call (ms) of ``fn(i)``: one pair of events, recorded
     on the stream the kernels run on, around n calls back to back (an event
@@ -505,6 +526,7 @@ def main():
                    "block_size": B, "pool_blocks_per_layer": wl.num_blocks, "layers_rotated": L,
                    "step": "kv_write + paged_attention_decode, one layer", "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "useful_kv_ratio": round(sum_ctx / float(((st.context_lens.astype(np.int64) + B - 1) // B * B).sum()), 5),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_us_avg": round(dec_avg * 1e3, 2),
@@ -567,7 +589,9 @@ def main():
             "kind": "oracle",
             "sample": f"the full {wl.name} batch (layer 0, {sum_ctx} context tokens) {runs} times in "
                       f"{t_cpu:.1f}s; numpy float64 on {platform.machine()}, os.cpu_count={os.cpu_count()}, "
-                      f"BLAS threads={cores}"}
+                      f"BLAS threads={cores}",
+            "seqs_per_s_per_layer": round(S * runs / t_cpu, 1),
+            "host": host_description(np)}
         result["parity_max_abs_err_vs_oracle"] = err
         log(f"oracle {t_cpu / runs:.2f}s per batch, decode parity max abs err {err:.3g}")
         if pf is not None:
@@ -576,6 +600,7 @@ def main():
             t1 = time.perf_counter()
             pexp = oracle_runner.expected(pwl, post)
             pf["cpu_oracle_s"] = round(time.perf_counter() - t1, 3)
+            pf["cpu_oracle_tflops"] = round(pf["algorithmic_gflop"] / pf["cpu_oracle_s"] / 1e3, 5)
             pf["parity_max_abs_err_vs_oracle"] = float(np.abs(driver.out_to_f64(pout) - pexp).max())
             log(f"prefill parity max abs err {pf['parity_max_abs_err_vs_oracle']:.3g}")
 
