@@ -347,9 +347,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // past 2^8 (a score above m by more than 8 in the log2 domain), or the
   // row has no reference yet, is the tile's true maximum taken, m raised
   // to it, the accumulators rescaled and the weights formed again.  So
-  // weights stay below 2^8 (bf16 and fp32 hold them exactly as scaled
-  // values), and the final division by the row sum, taken against the same
-  // references, cancels m exactly.  Masked keys (causal limit) occur only
+  // weights stay below 2^8, far inside the bf16 and fp32 range, and the
+  // final division by the row sum, taken against the same references,
+  // cancels m exactly.  Masked keys (causal limit) occur only
   // in the tiles on the wave's diagonal, which take the masked variant.
   const float c = a.scale_log2;
   auto softmax = [&](auto masked, int t0) __attribute__((always_inline)) {
