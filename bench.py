@@ -157,8 +157,7 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
     tflops = flops / (pf_ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
         f"{kw_ms * 1e3:.1f} us")
-    # the instantiation this shape runs (blocks of two or more tokens pair V rows)
-    kname = f"prefill_kernel<{D}, {'true' if B >= 2 else 'false'}>"
+    kname = f"prefill_kernel<{D}>"  # the instantiation this shape runs
     traffic = None
     mfma = {"mfma_util_pct": None, "executed_gflop": None}
     try:

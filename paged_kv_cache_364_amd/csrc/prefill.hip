@@ -11,9 +11,10 @@
 // Tiling.  A workgroup of eight wavefronts owns BM = 256 query rows of one
 // (sequence, head); wavefront w owns rows 32w .. 32w + 31.  Keys and values
 // are walked in tiles of KT = 64 tokens (several physical blocks gathered
-// through the table), double-buffered in LDS and staged through one set of
-// registers: the global loads of tile j + 2 are in flight while tile j is
-// computed.  The block-table entries the tiles need sit in an LDS window.
+// through the table), moved from global memory straight into LDS
+// (global_load_lds) and triple-buffered there: the transfers of tile j + 2
+// are in flight while tile j is computed.  The block-table entries the
+// tiles need sit in an LDS window.
 // Per tile and wavefront:
 //
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = the
@@ -22,12 +23,13 @@
 //                 and 16 keys in its registers, so the online-softmax state
 //                 (running max, running sum) of a query lives in one lane
 //                 pair (l, l ^ 32).
-//   O^T += V^T P^T  A = V^T from LDS, B = P^T taken straight from the S^T
+//   O^T += V^T P^T  A = V^T, B = P^T taken straight from the S^T
 //                 accumulators (converted to bf16): the keys a lane holds
-//                 in registers are exactly the contraction index the B
-//                 operand wants, provided V^T stores each 16-key group in
-//                 the order of that register layout.  V is written to LDS
-//                 transposed, in that order.
+//                 in registers are the contraction index the B operand
+//                 wants, so the A operand must hold the same keys of one
+//                 column d of V, in that order.  V stays row-major in LDS
+//                 and the transposing LDS read (ds_read_b64_tr_b16) builds
+//                 those fragments.
 //
 // A matrix-core contraction sums over its k index in any order, so the
 // assignment of keys (for O^T) or head dimensions (for S^T) to registers
@@ -43,6 +45,9 @@ namespace pkv {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 struct PrefillArgs {
   uint16_t* out;
@@ -64,26 +69,31 @@ constexpr int kPTableLds = 1024;  // block-table entries staged in LDS per workg
 
 template <int D>
 struct PShape {
-  static constexpr int KS = D / 16;          // contraction steps of S^T
-  static constexpr int DT = D / 32;          // 32-row tiles of O^T
-  static constexpr int PIECES = D / 8;       // 16-byte pieces per row
-  static constexpr int KROW = D + 8;         // K row in LDS (bf16), padded
-  static constexpr int VROW = kPKT + 8;      // V^T row in LDS (bf16), padded
-  static constexpr int K_ELEMS = kPKT * KROW;
-  static constexpr int V_ELEMS = D * VROW;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_TOTAL = kPKT * PIECES;                    // 16-byte K pieces per tile
-  static constexpr int V_TOTAL = (kPKT / 2) * PIECES;              // (2 keys x 16 bytes) V pieces per tile
-  static constexpr int K_LOADS = (K_TOTAL + kPThreads - 1) / kPThreads;  // per thread
-  static constexpr int V_PAIRS = (V_TOTAL + kPThreads - 1) / kPThreads;
+  static constexpr int KS = D / 16;                   // contraction steps of S^T
+  static constexpr int DT = D / 32;                   // 32-row tiles of O^T
+  static constexpr int PIECES = D / 8;                // 16-byte pieces per row
+  static constexpr int ROWB = D * 2;                  // bytes per K or V row
+  static constexpr int TILEB = kPKT * ROWB;           // bytes per tile and tensor
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / kPWaves;  // 1 KiB transfers per wavefront and tensor
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * 1024 * kPWaves == TILEB, "tile split");
 };
 
-// Position of key u (0..63) inside its 16-key group of a V^T row: the order
-// in which the S^T accumulator registers of a lane pair hold those keys.
-__device__ __forceinline__ int vt_pos(int u) {
-  const int v = u & 15;
-  return (u & ~15) + 8 * ((v >> 2) & 1) + 4 * (v >> 3) + (v & 3);
+// LDS layout of a K or V tile: row-major, 16-byte piece p of key `key` in
+// slot key * PIECES + (p ^ swz(key)).  The XOR spreads over all banks both
+// the K fragment reads (one piece of 16 consecutive keys per 16 lanes) and
+// the transposed V reads (4 pieces of 4 consecutive keys per 32 lanes).
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 128)
+    return ((key & 3) << 2) | ((key >> 2) & 3);
+  else
+    return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
 }
+
+// Rows for keys with no data: zeros past the context, NaN for a block id
+// outside the pool (so the rows that attend it come out NaN).
+__device__ __attribute__((aligned(16))) uint16_t g_pf_zero_row[128];
+__device__ __attribute__((aligned(16))) uint16_t g_pf_nan_row[128] = {0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0};
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v_t;
 
@@ -95,141 +105,80 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Workgroup barrier for the tile pipeline: this wavefront first waits until
+// at most N of its vector-memory operations are outstanding (the transfers
+// of the tile after next) and all its LDS operations are done, then meets
+// the others.  In the loop LDS is written only by the transfers and every
+// LDS read is consumed before the barrier, so no memory fence is needed:
+// a fence would also wait for the transfers still in flight.  The signal
+// fences only keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4):
+// lane l's bytes land at dst + 16 l, dst the same for the whole wavefront.
+// Written as assembly so that the compiler's wait-count pass, which cannot
+// tell which LDS buffer such a transfer writes, adds no wait for it before
+// every LDS read; tile_barrier waits for the transfers explicitly.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(m0), "v"(src)
+      : "memory", "m0");
+}
+
+// Issue the transfers of tile t0 .. t0 + 63 straight into LDS (K to kdst,
+// V to vdst): each 1 KiB transfer of a wavefront fills 64 consecutive
+// slots, lane l slot l, from the global piece that the swizzle puts there.
+// Block ids come from the workgroup's LDS window of the table (tbl[i] =
+// entry tbase + i); the entry is read unconditionally, index clamped into
+// the window, and a key past the context reads the zero row whatever the
+// entry holds.
 template <int D>
-struct TileRegs {
-  uint4 k[PShape<D>::K_LOADS];
-  uint4 v0[PShape<D>::V_PAIRS];
-  uint4 v1[PShape<D>::V_PAIRS];
-  uint32_t zero;  // bit per load: replace by zeros (key past the context)
-  uint32_t nan;   // bit per load: replace by NaN (block id outside the pool)
-};
-
-// Element offset of 16-byte piece `piece` of absolute key t of the sequence.
-// Every load is issued unconditionally from a valid address (block 0 when
-// the key has none) and flagged (code 1: key past the context, read as
-// zeros; code 2: block id outside the pool, read as NaN), so no branch sits
-// between a load and its use; the flags are applied when the tile is written
-// to LDS.  Block ids come from the workgroup's LDS window of the table:
-// tbl[i] = entry tbase + i.
-struct KeyPiece {
-  size_t off;
-  uint32_t code;
-};
-
-__device__ __forceinline__ KeyPiece key_piece(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t,
-                                              int ctx, int D, int piece) {
-  const bool in_ctx = t < ctx;
-  // The entry is read unconditionally (index clamped into the window) so
-  // that a tile's lookups issue together.  Past the context it may hold
-  // any value: any id inside the pool gives a valid address (the data is
-  // replaced by zeros), anything else falls back to block 0.
-  int blk = tbl[min((t >> a.log2B) - tbase, kPTableLds - 1)];
-  const bool outside = (unsigned)blk >= (unsigned)a.num_blocks;
-  blk = outside ? 0 : blk;
-  const uint32_t row = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
-  return {(size_t)row * D + piece * 8, (in_ctx ? 0u : 1u) | (in_ctx && outside ? 2u : 0u)};
-}
-
-__device__ __forceinline__ uint4 apply_fill(uint4 v, uint32_t zero, uint32_t nan, int bit) {
-  if ((zero >> bit) & 1) v = make_uint4(0, 0, 0, 0);
-  if ((nan >> bit) & 1) v = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-  return v;
-}
-
-template <int D, bool PAIRED>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillArgs& a, const int* tbl, int tbase, int kvh,
-                                          int t0, int ctx, int tid) {
+__device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t0, int ctx,
+                                         int wave, int lane, uint8_t* kdst, uint8_t* vdst) {
   using PS = PShape<D>;
-  r.zero = 0;
-  r.nan = 0;
 #pragma unroll
-  for (int n = 0; n < PS::K_LOADS; ++n) {
-    const int idx = tid + n * kPThreads;
-    if (PS::K_TOTAL % kPThreads != 0 && idx >= PS::K_TOTAL) break;
-    const int key = idx / PS::PIECES;
-    const int pc = idx % PS::PIECES;
-    const KeyPiece kp = key_piece(a, tbl, tbase, kvh, t0 + key, ctx, D, pc);
-    r.k[n] = *(const uint4*)(a.k_cache + kp.off);
-    r.zero |= (kp.code & 1u) << n;
-    r.nan |= (kp.code >> 1) << n;
-  }
-#pragma unroll
-  for (int n = 0; n < PS::V_PAIRS; ++n) {
-    const int idx = tid + n * kPThreads;
-    if (PS::V_TOTAL % kPThreads != 0 && idx >= PS::V_TOTAL) break;
-    const int pair = idx % (kPKT / 2);
-    const int pc = idx / (kPKT / 2);
-    const int b0 = PS::K_LOADS + 2 * n;
-    const KeyPiece p0 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair, ctx, D, pc);
-    KeyPiece p1;
-    if constexpr (PAIRED) {
-      // blocks of two or more tokens: keys 2 * pair and 2 * pair + 1 share
-      // a block, so the second row follows the first
-      const bool in1 = t0 + 2 * pair + 1 < ctx;
-      p1 = {p0.off + D, (in1 ? 0u : 1u) | (in1 && (p0.code & 3u) == 2u ? 2u : 0u)};
-    } else {
-      p1 = key_piece(a, tbl, tbase, kvh, t0 + 2 * pair + 1, ctx, D, pc);
-    }
-    r.v0[n] = *(const uint4*)(a.v_cache + p0.off);
-    r.v1[n] = *(const uint4*)(a.v_cache + p1.off);
-    r.zero |= ((p0.code & 1u) << b0) | ((p1.code & 1u) << (b0 + 1));
-    r.nan |= ((p0.code >> 1) << b0) | ((p1.code >> 1) << (b0 + 1));
+  for (int i = 0; i < PS::DMA_PER_WAVE; ++i) {
+    const int g = wave * PS::DMA_PER_WAVE + i;  // 1 KiB chunk of the tile
+    const int sl = g * 64 + lane;               // 16-byte slot
+    const int key = sl / PS::PIECES;
+    const int p = (sl % PS::PIECES) ^ swz<D>(key);
+    const int t = t0 + key;
+    const bool in_ctx = t < ctx;
+    const int blk = tbl[min((t >> a.log2B) - tbase, kPTableLds - 1)];
+    const bool outside = (unsigned)blk >= (unsigned)a.num_blocks;
+    const uint32_t row =
+        (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
+    const size_t off = (size_t)row * D + p * 8;
+    const bool real = in_ctx && !outside;
+    const uint16_t* fill = in_ctx ? g_pf_nan_row + p * 8 : g_pf_zero_row + p * 8;  // used when !real
+    const uint16_t* ksrc = real ? a.k_cache + off : fill;
+    const uint16_t* vsrc = real ? a.v_cache + off : fill;
+    lds_dma16(ksrc, kdst + g * 1024);
+    lds_dma16(vsrc, vdst + g * 1024);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* kl, uint16_t* vl, int tid) {
-  using PS = PShape<D>;
-  uint4 kx[PS::K_LOADS], v0x[PS::V_PAIRS], v1x[PS::V_PAIRS];
-#pragma unroll
-  for (int n = 0; n < PS::K_LOADS; ++n) kx[n] = r.k[n];
-#pragma unroll
-  for (int n = 0; n < PS::V_PAIRS; ++n) {
-    v0x[n] = r.v0[n];
-    v1x[n] = r.v1[n];
-  }
-  // zero / NaN fills are needed only past the context end or for bad block
-  // ids: skipped (one scalar branch) unless some lane of the wave has one
-  if (__builtin_amdgcn_ballot_w64((r.zero | r.nan) != 0u)) {
-#pragma unroll
-    for (int n = 0; n < PS::K_LOADS; ++n) kx[n] = apply_fill(kx[n], r.zero, r.nan, n);
-#pragma unroll
-    for (int n = 0; n < PS::V_PAIRS; ++n) {
-      v0x[n] = apply_fill(v0x[n], r.zero, r.nan, PS::K_LOADS + 2 * n);
-      v1x[n] = apply_fill(v1x[n], r.zero, r.nan, PS::K_LOADS + 2 * n + 1);
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < PS::K_LOADS; ++n) {
-    const int idx = tid + n * kPThreads;
-    if (PS::K_TOTAL % kPThreads != 0 && idx >= PS::K_TOTAL) break;
-    const int key = idx / PS::PIECES;
-    const int pc = idx % PS::PIECES;
-    *(uint4*)(kl + key * PS::KROW + pc * 8) = kx[n];
-  }
-#pragma unroll
-  for (int n = 0; n < PS::V_PAIRS; ++n) {
-    const int idx = tid + n * kPThreads;
-    if (PS::V_TOTAL % kPThreads != 0 && idx >= PS::V_TOTAL) break;
-    const int pair = idx % (kPKT / 2);
-    const int pc = idx / (kPKT / 2);
-    const int pos = vt_pos(2 * pair);  // even; key 2 * pair + 1 sits next to it
-    const uint32_t a0[4] = {v0x[n].x, v0x[n].y, v0x[n].z, v0x[n].w};
-    const uint32_t a1[4] = {v1x[n].x, v1x[n].y, v1x[n].z, v1x[n].w};
-    // element e of key 2 * pair (low half) and of key 2 * pair + 1 (high
-    // half) in one v_perm_b32: byte selectors 0-3 pick from a0, 4-7 from a1
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *(uint32_t*)(vl + (pc * 8 + e) * PS::VROW + pos) =
-          __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-  }
-}
-
-template <int D, bool PAIRED>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t klds[2 * PS::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[2 * PS::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[PS::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[PS::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb2[PS::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[PS::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[PS::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb2[PS::TILEB];
   __shared__ int tbl[kPTableLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,6 +224,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       const uint4 v = row_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
       qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
+    // all query rows in registers before the first tile transfer: the
+    // compiler then never waits for them (and for the transfers behind
+    // them) inside the loop
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   }
 
   f32x16_t acc_o[PS::DT];
@@ -298,7 +251,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   fill_window(0);
   __syncthreads();
 
-  auto load = [&](TileRegs<D>& r, int jt) __attribute__((always_inline)) {
+  // three LDS buffers per tensor, picked at compile time (the loop below is
+  // unrolled by three) so that reads of one are told apart from transfers
+  // into another
+  auto kbuf = [&](auto r) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int R = decltype(r)::value;
+    if constexpr (R == 0) return kb0;
+    else if constexpr (R == 1) return kb1;
+    else return kb2;
+  };
+  auto vbuf = [&](auto r) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int R = decltype(r)::value;
+    if constexpr (R == 0) return vb0;
+    else if constexpr (R == 1) return vb1;
+    else return vb2;
+  };
+  auto dma = [&](int jt, auto r) __attribute__((always_inline)) {
     // slide the window when tile jt leaves it (uniform over the workgroup)
     const int last_blk = (min((jt + 1) * kPKT, ctx) - 1) >> a.log2B;
     if (last_blk >= tbase + kPTableLds) {
@@ -307,31 +275,33 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       fill_window(tbase);
       __syncthreads();
     }
-    load_tile<D, PAIRED>(r, a, tbl, tbase, kvh, jt * kPKT, ctx, tid);
+    dma_tile<D>(a, tbl, tbase, kvh, jt * kPKT, ctx, wave, lane, kbuf(r), vbuf(r));
   };
   auto live = [&](int j) __attribute__((always_inline)) { return wave_live && j * kPKT <= wave_last_pos; };
 
   // S^T for keys 64j .. 64j + 63 (two 32-key tiles) x this wave's 32
   // queries.  The two accumulators alternate; the K fragments are read two
   // contraction steps ahead, in an order the scheduler may not sink.
-  auto s_phase = [&](int j) __attribute__((always_inline)) {
-    const uint16_t* k0 = klds + (j & 1) * PS::K_ELEMS + lq * PS::KROW + hh * 8;
-    const uint16_t* k1 = k0 + 32 * PS::KROW;
+  const int ksw = swz<D>(lq);  // rows lq and lq + 32 share it
+  auto s_phase = [&](auto r) __attribute__((always_inline)) {
+    const uint8_t* k0 = kbuf(r) + lq * PS::ROWB;
+    const uint8_t* k1 = k0 + 32 * PS::ROWB;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      for (int rr = 0; rr < 16; ++rr) sacc[mt][rr] = 0.f;
     uint4 f0[PS::KS], f1[PS::KS];
-    f0[0] = *(const uint4*)k0;
-    f1[0] = *(const uint4*)k1;
-    f0[1] = *(const uint4*)(k0 + 16);
-    f1[1] = *(const uint4*)(k1 + 16);
+    auto kofs = [&](int ks) __attribute__((always_inline)) { return ((2 * ks + hh) ^ ksw) << 4; };
+    f0[0] = *(const uint4*)(k0 + kofs(0));
+    f1[0] = *(const uint4*)(k1 + kofs(0));
+    f0[1] = *(const uint4*)(k0 + kofs(1));
+    f1[1] = *(const uint4*)(k1 + kofs(1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < PS::KS; ++ks) {
       if (ks + 2 < PS::KS) {
-        f0[ks + 2] = *(const uint4*)(k0 + (ks + 2) * 16);
-        f1[ks + 2] = *(const uint4*)(k1 + (ks + 2) * 16);
+        f0[ks + 2] = *(const uint4*)(k0 + kofs(ks + 2));
+        f1[ks + 2] = *(const uint4*)(k1 + kofs(ks + 2));
       }
       __builtin_amdgcn_sched_barrier(0);
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[ks]), qreg[ks], sacc[0], 0, 0, 0);
@@ -424,18 +394,41 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       softmax(std::false_type{}, t0);
   };
 
-  // O^T += V^T P^T: the DT accumulators alternate; the V^T fragments of the
-  // next contraction step are read while this step's products run
-  auto o_phase = [&](int j) __attribute__((always_inline)) {
-    const uint16_t* v0 = vlds + (j & 1) * PS::V_ELEMS + lq * PS::VROW + hh * 8;
-    uint4 fa[PS::DT], fb[PS::DT];
+  // O^T += V^T P^T.  The A operand (row d, 8 keys in the order the S^T
+  // accumulator holds them) comes from the row-major V tile through two
+  // transposed reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+  // i names 4 columns d0 + 4 (i % 4) .. + 3 of key k0 + i / 4, and lane j
+  // receives column d0 + j of keys k0 .. k0 + 3.  Byte offsets per lane for
+  // each 32-row tile dt and key half h2 of a 16-key step:
+  int vofs[PS::DT][2];
+  {
+    const int i16 = lane & 15, g16 = (lane >> 4) & 1;
 #pragma unroll
-    for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW);
+    for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int key = 8 * h2 + 4 * hh + (i16 >> 2);  // + 16 and 32 multiples: same swizzle
+        const int p = 4 * dt + 2 * g16 + ((i16 & 3) >> 1);
+        vofs[dt][h2] = key * PS::ROWB + ((p ^ swz<D>(key)) << 4) + ((i16 & 1) << 3);
+      }
+  }
+  auto o_phase = [&](auto r) __attribute__((always_inline)) {
+    const uint8_t* vb = vbuf(r);
+    auto vfrag = [&](int dt, int kk) __attribute__((always_inline)) {
+      const int ko = (32 * (kk >> 1) + 16 * (kk & 1)) * PS::ROWB;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vofs[dt][0] + ko));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + vofs[dt][1] + ko));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8_t;
+    s16x8_t fa[PS::DT], fb[PS::DT];
+#pragma unroll
+    for (int dt = 0; dt < PS::DT; ++dt) fa[dt] = vfrag(dt, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk + 1 < 4) {
 #pragma unroll
-        for (int dt = 0; dt < PS::DT; ++dt) fb[dt] = *(const uint4*)(v0 + dt * 32 * PS::VROW + (kk + 1) * 16);
+        for (int dt = 0; dt < PS::DT; ++dt) fb[dt] = vfrag(dt, kk + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -448,30 +441,39 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // Key tiles flow global -> registers -> LDS through one register stage,
-  // double buffered in LDS: step j first writes tile j + 1 (loaded during
-  // step j - 1) over tile j - 1, then issues the loads of tile j + 2 into the
-  // same registers, then computes tile j, so a tile's loads have a whole
-  // step of compute to arrive.
-  TileRegs<D> rg;
-  auto step = [&](int j) __attribute__((always_inline)) {
-    if (j + 1 < n_tiles) {
-      store_tile<D>(rg, klds + ((j + 1) & 1) * PS::K_ELEMS, vlds + ((j + 1) & 1) * PS::V_ELEMS, tid);
-      if (j + 2 < n_tiles) load(rg, j + 2);
-    }
+  // Tiles go from global memory straight into LDS, three buffers deep:
+  // step j issues the transfers of tile j + 2, computes tile j, then waits
+  // for its own share of tile j + 1 (issued one step earlier) and meets the
+  // other wavefronts at the barrier, after which tile j + 1 is whole.
+  // Tile j + 2 goes over tile j - 1, which every wavefront finished before
+  // the previous barrier.
+  auto step = [&](int j, auto r) __attribute__((always_inline)) {
+    constexpr int R = decltype(r)::value;
+    const bool more = j + 2 < n_tiles;
+    if (more) dma(j + 2, std::integral_constant<int, (R + 2) % 3>{});
     if (live(j)) {
-      s_phase(j);
+      s_phase(r);
       sm_phase(j);
-      o_phase(j);
+      o_phase(r);
     }
-    __syncthreads();
+    if (more)
+      tile_barrier<2 * PS::DMA_PER_WAVE>();
+    else
+      tile_barrier<0>();
   };
 
-  load(rg, 0);
-  store_tile<D>(rg, klds, vlds, tid);
-  if (n_tiles > 1) load(rg, 1);
-  __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) step(j);
+  dma(0, std::integral_constant<int, 0>{});
+  if (n_tiles > 1) {
+    dma(1, std::integral_constant<int, 1>{});
+    tile_barrier<2 * PS::DMA_PER_WAVE>();
+  } else {
+    tile_barrier<0>();
+  }
+  for (int j = 0; j < n_tiles; j += 3) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < n_tiles) step(j + 2, std::integral_constant<int, 2>{});
+  }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
@@ -522,14 +524,10 @@ int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total
   if (grid <= 0) return 0;
   if (grid > 0x7fffffffLL) return -2;
   const dim3 g((unsigned)grid), b(kPThreads);
-  if (D == 128 && B >= 2)
-    hipLaunchKernelGGL((prefill_kernel<128, true>), g, b, 0, stream, a);
-  else if (D == 128)
-    hipLaunchKernelGGL((prefill_kernel<128, false>), g, b, 0, stream, a);
-  else if (D == 64 && B >= 2)
-    hipLaunchKernelGGL((prefill_kernel<64, true>), g, b, 0, stream, a);
+  if (D == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, g, b, 0, stream, a);
   else if (D == 64)
-    hipLaunchKernelGGL((prefill_kernel<64, false>), g, b, 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, g, b, 0, stream, a);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -6;
