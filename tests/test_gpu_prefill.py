@@ -123,3 +123,26 @@ def test_prefill_out_of_range_block_gives_nan_rows_only():
     o = out.float()
     assert torch.isfinite(o[:32]).all()
     assert torch.isnan(o[32:]).all()
+
+
+def test_prefill_ignores_table_padding():
+    """Entries past a sequence's last block may hold anything (in-pool ids,
+    ids outside the pool, negatives): the outputs are bitwise those of the
+    table padded with -1."""
+    wl = small("pf-padding", 88, [37, 5, 0], [20, 70, 33], 4, 2, 128, 16, num_blocks=64)
+    st = driver.run_script(wl)
+    q = driver.to_device(wl.q, "bf16", "cuda")
+    cu = torch.from_numpy(driver.cu_lens(wl.q_lens)).cuda()
+    scale = float(wl.scale)
+    ref = torch.empty_like(q)
+    api.paged_attention_prefill(ref, q, cu, max(wl.q_lens), st.k_pool, st.v_pool, st.tables_dev, st.lens_dev, scale)
+    tb = st.tables_dev.clone()
+    junk = torch.tensor([3, 1 << 30, -7, 63, 0, -1, 2 ** 31 - 1], dtype=torch.int32, device="cuda")
+    for s in range(tb.shape[0]):
+        used = -(-int(st.context_lens[s]) // wl.block_size)
+        for i in range(used, tb.shape[1]):
+            tb[s, i] = junk[(s + i) % junk.numel()]
+    out = torch.empty_like(q)
+    api.paged_attention_prefill(out, q, cu, max(wl.q_lens), st.k_pool, st.v_pool, tb, st.lens_dev, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
