@@ -8,18 +8,25 @@
 // here with the running-max online softmax, so the result is the plain
 // softmax(scale * Q K^T) V of the pages (cnblogs section 6).
 //
-// Tiling.  A workgroup of eight wavefronts owns BM = 256 query rows of one
-// (sequence, head); wavefront w owns rows 32w .. 32w + 31.  Keys and values
-// are walked in tiles of KT = 64 tokens (several physical blocks gathered
-// through the table), moved from global memory straight into LDS
-// (global_load_lds) and triple-buffered there: the transfers of tile j + 2
-// are in flight while tile j is computed.  The block-table entries the
-// tiles need sit in an LDS window.
+// Tiling.  A workgroup of eight wavefronts computes BM = 256 query rows of
+// one (sequence, head) at a time; wavefront w owns rows 32w .. 32w + 31.
+// Keys and values are walked in tiles of KT = 64 tokens (several physical
+// blocks gathered through the table), moved from global memory straight
+// into LDS (global_load_lds) and triple-buffered there: the transfers of
+// tile j + 2 are in flight while tile j is computed.  The query rows sit in
+// LDS too, laid out like a K tile.
+//
+// Schedule.  The grid is persistent, one workgroup per compute unit.  A
+// workgroup walks its share of the (sequence, head, q tile) items as one
+// stream of key tiles, so the transfers run on across the end of an item
+// and the next item's query rows load while the current item's last tile
+// is computed: no workgroup start-up or drain between items.
+//
 // Per tile and wavefront:
 //
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = the
-//                 wavefront's query rows, held in registers for the whole
-//                 loop.  The accumulator layout puts query l % 32 on lane l
+//                 wavefront's query rows from LDS.  The accumulator layout
+//                 puts query l % 32 on lane l
 //                 and 16 keys in its registers, so the online-softmax state
 //                 (running max, running sum) of a query lives in one lane
 //                 pair (l, l ^ 32).
@@ -65,7 +72,6 @@ constexpr int kPWaves = 8;                 // wavefronts per workgroup, 32 query
 constexpr int kPBM = 32 * kPWaves;         // query rows per workgroup
 constexpr int kPKT = 64;                   // keys per tile
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kPTableLds = 1024;  // block-table entries staged in LDS per workgroup
 
 template <int D>
 struct PShape {
@@ -137,98 +143,245 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
       : "memory", "m0");
 }
 
+// The same transfer with a wavefront-uniform 64-bit base in SGPRs and a
+// 32-bit per-lane byte offset (the instruction's saddr form).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint8_t* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(m0), "v"(voff), "s"(sbase)
+      : "memory", "m0");
+}
+
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// Table entry i of a row, read through the scalar cache when i is the same
+// for the whole wavefront (the table does not change during the kernel).
+__device__ __forceinline__ int table_entry(const int32_t* trow, int i) { return ((const_i32_t*)trow)[i]; }
+
+// Transfer g of tile t0 .. t0 + 63 in the general form: every lane finds
+// its own key, block and source.  Used only when a block holds fewer keys
+// than one transfer covers.  The entry is read with its index clamped into
+// the row, and a key past the context reads the zero row whatever the entry
+// holds.
+template <int D>
+__device__ __forceinline__ void dma_lanes(const PrefillArgs& a, const int32_t* trow, int kvh, int t0, int ctx, int g,
+                                          int lane, uint8_t* kdst, uint8_t* vdst) {
+  using PS = PShape<D>;
+  const int sl = g * 64 + lane;  // 16-byte slot
+  const int key = sl / PS::PIECES;
+  const int p = (sl % PS::PIECES) ^ swz<D>(key);
+  const int t = t0 + key;
+  const bool in_ctx = t < ctx;
+  const int blk = trow[min(t >> a.log2B, a.max_blocks - 1)];
+  const bool outside = (unsigned)blk >= (unsigned)a.num_blocks;
+  const uint32_t row =
+      (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
+  const size_t off = (size_t)row * D + p * 8;
+  const bool real = in_ctx && !outside;
+  const uint16_t* fill = in_ctx ? g_pf_nan_row + p * 8 : g_pf_zero_row + p * 8;  // used when !real
+  const uint16_t* ksrc = real ? a.k_cache + off : fill;
+  const uint16_t* vsrc = real ? a.v_cache + off : fill;
+  lds_dma16(ksrc, kdst + g * 1024);
+  lds_dma16(vsrc, vdst + g * 1024);
+}
+
+// Per-lane byte offset of transfer g inside its block, from the block's row
+// (t0 mod B): the same for every tile, so it is computed once.  A transfer
+// covers 64 / PIECES consecutive keys, which lie in one block when the
+// block holds at least that many.
+template <int D>
+__device__ __forceinline__ uint32_t dma_lane_offset(int g, int lane, int log2B) {
+  using PS = PShape<D>;
+  const int sl = g * 64 + lane;
+  const int key = sl / PS::PIECES;
+  const int p = (sl % PS::PIECES) ^ swz<D>(key);
+  return (uint32_t)(((key & ((1 << log2B) - 1)) * D + p * 8) * 2);
+}
+
+// Block ids of this wavefront's transfers of tile t0 (one per transfer;
+// index clamped into the row, so an entry past the table is never read).
+template <int D>
+struct TileEntries {
+  int e[PShape<D>::DMA_PER_WAVE];
+};
+template <int D>
+__device__ __forceinline__ TileEntries<D> tile_entries(const PrefillArgs& a, const int32_t* trow, int t0, int wave) {
+  using PS = PShape<D>;
+  constexpr int KPX = 64 / PS::PIECES;
+  TileEntries<D> r;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: a scalar load
+#pragma unroll
+  for (int i = 0; i < PS::DMA_PER_WAVE; ++i) {
+    const int g = wv * PS::DMA_PER_WAVE + i;
+    r.e[i] = table_entry(trow, min((t0 + g * KPX) >> a.log2B, a.max_blocks - 1));
+  }
+  return r;
+}
+
 // Issue the transfers of tile t0 .. t0 + 63 straight into LDS (K to kdst,
 // V to vdst): each 1 KiB transfer of a wavefront fills 64 consecutive
 // slots, lane l slot l, from the global piece that the swizzle puts there.
-// Block ids come from the workgroup's LDS window of the table (tbl[i] =
-// entry tbase + i); the entry is read unconditionally, index clamped into
-// the window, and a key past the context reads the zero row whatever the
-// entry holds.
+// When a block holds at least the 64 / PIECES keys of a transfer, the
+// transfer's block id (ent, read ahead through the scalar cache) gives the
+// block's address in SGPRs and the lanes add their fixed offsets (voff).
+// Keys past the context read the zero row and a block id outside the pool
+// reads the NaN row; those cases pick a source per lane.
 template <int D>
-__device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int* tbl, int tbase, int kvh, int t0, int ctx,
-                                         int wave, int lane, uint8_t* kdst, uint8_t* vdst) {
+__device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int32_t* trow, const TileEntries<D>& ent,
+                                         int kvh, int t0, int ctx, int wave, int lane, const uint32_t* voff,
+                                         uint8_t* kdst, uint8_t* vdst) {
   using PS = PShape<D>;
+  constexpr int KPX = 64 / PS::PIECES;  // keys per transfer
+  const bool whole = t0 + kPKT <= ctx;
 #pragma unroll
   for (int i = 0; i < PS::DMA_PER_WAVE; ++i) {
     const int g = wave * PS::DMA_PER_WAVE + i;  // 1 KiB chunk of the tile
-    const int sl = g * 64 + lane;               // 16-byte slot
-    const int key = sl / PS::PIECES;
-    const int p = (sl % PS::PIECES) ^ swz<D>(key);
-    const int t = t0 + key;
-    const bool in_ctx = t < ctx;
-    const int blk = tbl[min((t >> a.log2B) - tbase, kPTableLds - 1)];
-    const bool outside = (unsigned)blk >= (unsigned)a.num_blocks;
-    const uint32_t row =
-        (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
-    const size_t off = (size_t)row * D + p * 8;
-    const bool real = in_ctx && !outside;
-    const uint16_t* fill = in_ctx ? g_pf_nan_row + p * 8 : g_pf_zero_row + p * 8;  // used when !real
-    const uint16_t* ksrc = real ? a.k_cache + off : fill;
-    const uint16_t* vsrc = real ? a.v_cache + off : fill;
-    lds_dma16(ksrc, kdst + g * 1024);
-    lds_dma16(vsrc, vdst + g * 1024);
+    if ((1 << a.log2B) < KPX) {
+      dma_lanes<D>(a, trow, kvh, t0, ctx, g, lane, kdst, vdst);
+      continue;
+    }
+    const int blk = ent.e[i];
+    const bool valid = (unsigned)blk < (unsigned)a.num_blocks;
+    const uint32_t row0 =
+        (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t0 & ((1 << a.log2B) - 1));
+    const size_t boff = (size_t)row0 * PS::ROWB;
+    if (whole && valid) {
+      lds_dma16_s((const uint8_t*)a.k_cache + boff, voff[i], kdst + g * 1024);
+      lds_dma16_s((const uint8_t*)a.v_cache + boff, voff[i], vdst + g * 1024);
+    } else {
+      // an opaque copy of the lane index keeps the compiler from hoisting
+      // this rarely taken path's per-lane values out of the loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int sl = g * 64 + ln;
+      const int key = sl / PS::PIECES;
+      const int p = (sl % PS::PIECES) ^ swz<D>(key);
+      const bool in_ctx = t0 + key < ctx;
+      const uint8_t* fill = (const uint8_t*)(in_ctx ? g_pf_nan_row : g_pf_zero_row) + p * 16;
+      const bool real = in_ctx && valid;
+      lds_dma16(real ? (const uint8_t*)a.k_cache + boff + voff[i] : fill, kdst + g * 1024);
+      lds_dma16(real ? (const uint8_t*)a.v_cache + boff + voff[i] : fill, vdst + g * 1024);
+    }
   }
 }
 
+// One (sequence, head, q tile) of a workgroup's share, as the two cursors
+// of the tile stream see it.  k < 0: the share is exhausted.
+struct PItem {
+  int k;                // position in the workgroup's share
+  int h, kvh, qbeg, C, P, ctx, q0, n_tiles;
+  const int32_t* trow;  // the sequence's block-table row
+};
+
+// Key tiles that all q tiles of sequence s walk: the work it brings.
+__device__ __forceinline__ int seq_tiles(const PrefillArgs& a, int s) {
+  const int C = a.cu_q_lens[s + 1] - a.cu_q_lens[s];
+  const int P = min(a.ctx_lens[s], a.max_blocks << a.log2B) - C;
+  int n = 0;
+  for (int q0 = 0; q0 < C; q0 += kPBM) n += max((P + min(C, q0 + kPBM) - 1) / kPKT + 1, 1);
+  return n;
+}
+
+// Persistent grid.  Every workgroup walks a share of the work items
+// (sequence, head, q tile) as one stream of key tiles: the transfers run two
+// tiles ahead of the computation, across the end of an item, and the next
+// item's query rows move into LDS while the last tile of the current one is
+// computed.  Sequences are ranked by their number of key tiles, heaviest
+// first (batches of at most 64 sequences; larger ones keep batch order), and
+// the items of a round of gridDim.x go out in snake order (reversed every
+// other round) so that the heavy ones spread evenly; consecutive items (the
+// q tiles and heads of one sequence) go to workgroups on one XCD, which then
+// share its L2 for the keys and values.
 template <int D>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   using PS = PShape<D>;
+  constexpr int QX = 32 * PS::ROWB / 1024;  // 1 KiB query transfers per wavefront
   __shared__ __attribute__((aligned(1024))) uint8_t kb0[PS::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t kb1[PS::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t kb2[PS::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[PS::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[PS::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vb2[PS::TILEB];
-  __shared__ int tbl[kPTableLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t qb[kPBM * PS::ROWB];  // query rows, laid out like K
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hh = lane >> 5;  // lane half
   const int lq = lane & 31;
 
-  // Workgroup -> (unit, q tile).  Workgroups are dealt to the 8 XCDs round
-  // robin; all q tiles of one (sequence, head) go to one XCD, one after the
-  // other and heaviest (last) first, so they share its L2 for the keys and
-  // values, and consecutive units spread over the XCDs.
-  const int f = blockIdx.x;
-  const int xcd = f & 7;
-  const int k = f >> 3;
-  const int unit = (k / a.q_tiles) * 8 + xcd;
-  const int qt = a.q_tiles - 1 - (k % a.q_tiles);
-  if (unit >= a.S * a.Hq) return;
-  const int s = unit / a.Hq;
-  const int h = unit - s * a.Hq;
-  const int kvh = h / a.G;
-  const int qbeg = a.cu_q_lens[s];
-  const int C = a.cu_q_lens[s + 1] - qbeg;
-  const int q0 = qt * kPBM;
-  if (q0 >= C) return;
-  const int ctx = min(a.ctx_lens[s], a.max_blocks << a.log2B);  // never past the table
-  const int P = ctx - C;  // cached prefix length
-  const int rows_end = min(C, q0 + kPBM);
-  const int n_tiles = (P + rows_end - 1) / kPKT + 1;  // keys 0 .. P + rows_end - 1
-  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
-
-  // this wavefront's query rows and their B operands (query l % 32)
-  const int wr0 = q0 + wave * 32;
-  const bool wave_live = wr0 < C;
-  const int my_row = wr0 + lq;
-  const bool row_ok = my_row < C;
-  const int my_pos = P + my_row;
-  const int wave_last_pos = P + min(wr0 + 31, C - 1);
-  bf16x8_t qreg[PS::KS];
-  {
-    const uint16_t* qp = a.q + ((size_t)(qbeg + min(my_row, C - 1)) * a.Hq + h) * D + hh * 8;
-#pragma unroll
-    for (int ks = 0; ks < PS::KS; ++ks) {
-      const uint4 v = row_ok ? *(const uint4*)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+  // Lane r of ordv holds the sequence of rank r.
+  const bool ranked = a.S <= 64;
+  int ordv = lane;
+  if (ranked) {
+    const int cs = lane < a.S ? seq_tiles(a, lane) : -1;
+    int rank = 0;
+    for (int t = 0; t < a.S; ++t) {
+      const int ct = __shfl(cs, t);
+      rank += (ct > cs) | ((ct == cs) & (t < lane));
     }
-    // all query rows in registers before the first tile transfer: the
-    // compiler then never waits for them (and for the transfers behind
-    // them) inside the loop
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    ordv = __builtin_amdgcn_ds_permute(min(rank, 63) * 4, lane);
   }
+  const int G = gridDim.x;
+  const int per_seq = a.Hq * a.q_tiles;
+  const int n_items = a.S * per_seq;
+  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int maxctx = a.max_blocks << a.log2B;
+
+  // The first item with work at or after position k of the share.
+  auto item_at = [&](int k) __attribute__((always_inline)) {
+    PItem it;
+    for (;; ++k) {
+      const int i = k * G + ((k & 1) ? G - 1 - slot : slot);
+      if (i >= n_items) {
+        it.k = -1;
+        return it;
+      }
+      const int c = i / per_seq;
+      const int rem = i - c * per_seq;
+      const int h = rem / a.q_tiles;
+      const int qt = a.q_tiles - 1 - (rem - h * a.q_tiles);  // heavier q tile first
+      const int s = ranked ? __builtin_amdgcn_readlane(ordv, c) : c;
+      const int qbeg = a.cu_q_lens[s];
+      const int C = a.cu_q_lens[s + 1] - qbeg;
+      const int q0 = qt * kPBM;
+      if (q0 >= C) continue;
+      it.k = k;
+      it.h = h;
+      it.kvh = h / a.G;
+      it.qbeg = qbeg;
+      it.C = C;
+      it.ctx = min(a.ctx_lens[s], maxctx);  // never past the table
+      it.P = it.ctx - C;                     // cached prefix length
+      it.q0 = q0;
+      it.n_tiles = max((it.P + min(C, q0 + kPBM) - 1) / kPKT + 1, 1);  // keys 0 .. P + last row
+      it.trow = a.tables + (size_t)s * a.max_blocks;
+      return it;
+    }
+  };
+
+  PItem ci = item_at(0);  // item being computed
+  if (ci.k < 0) return;
+  PItem nci = item_at(ci.k + 1);  // the one after it
+  PItem di = ci;                  // item of the next tile to transfer
+  int tc = 0, td = 0;             // tile of ci being computed, of di to transfer next
+
+  // this wavefront's query rows of item ci
+  int wr0, my_row, my_pos, wave_last_pos, P;
+  bool wave_live, row_ok;
+  auto set_rows = [&]() __attribute__((always_inline)) {
+    P = ci.P;
+    wr0 = ci.q0 + wave * 32;
+    wave_live = wr0 < ci.C;
+    my_row = wr0 + lq;
+    row_ok = my_row < ci.C;
+    my_pos = P + my_row;
+    wave_last_pos = P + min(wr0 + 31, ci.C - 1);
+  };
+  set_rows();
 
   f32x16_t acc_o[PS::DT];
 #pragma unroll
@@ -239,17 +392,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   f32x16_t sacc[2];
   bf16x8_t pb[4];
 
-  // Block-table window in LDS: entries tbase .. tbase + kPTableLds - 1 of
-  // the sequence's row (those the tiles need; keys past the causal limit
-  // are loaded too, then masked, so whole tiles must map to real blocks).
-  const int nblk_all = (min(ctx, n_tiles * kPKT) + (1 << a.log2B) - 1) >> a.log2B;
-  int tbase = 0;
-  auto fill_window = [&](int base) __attribute__((always_inline)) {
-    const int n = min(nblk_all - base, kPTableLds);
-    for (int i = tid; i < n; i += kPThreads) tbl[i] = trow[base + i];
-  };
-  fill_window(0);
-  __syncthreads();
+  // fixed per-lane offsets of the short-form transfers
+  uint32_t voff[PS::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PS::DMA_PER_WAVE; ++i) voff[i] = dma_lane_offset<D>(wave * PS::DMA_PER_WAVE + i, lane, a.log2B);
 
   // three LDS buffers per tensor, picked at compile time (the loop below is
   // unrolled by three) so that reads of one are told apart from transfers
@@ -266,16 +412,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     else if constexpr (R == 1) return vb1;
     else return vb2;
   };
-  auto dma = [&](int jt, auto r) __attribute__((always_inline)) {
-    // slide the window when tile jt leaves it (uniform over the workgroup)
-    const int last_blk = (min((jt + 1) * kPKT, ctx) - 1) >> a.log2B;
-    if (last_blk >= tbase + kPTableLds) {
-      __syncthreads();
-      tbase = (jt * kPKT) >> a.log2B;
-      fill_window(tbase);
-      __syncthreads();
+  // transfer tile td of item di, then move that cursor on
+  TileEntries<D> ent;  // block ids of tile td of di
+  auto entries = [&]() __attribute__((always_inline)) { return tile_entries<D>(a, di.trow, td * kPKT, wave); };
+  auto dma_next = [&](auto r) __attribute__((always_inline)) {
+    dma_tile<D>(a, di.trow, ent, di.kvh, td * kPKT, di.ctx, wave, lane, voff, kbuf(r), vbuf(r));
+    if (++td == di.n_tiles) {
+      di = item_at(di.k + 1);
+      td = 0;
     }
-    dma_tile<D>(a, tbl, tbase, kvh, jt * kPKT, ctx, wave, lane, kbuf(r), vbuf(r));
+    if (di.k >= 0) ent = entries();  // arrives while a tile is computed
+  };
+  // this wavefront's 32 query rows of item it into LDS (rows past the
+  // chunk repeat its last row; their outputs are not stored)
+  auto q_dma = [&](const PItem& it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < QX; ++x) {
+      const int sl = x * 64 + lane;
+      const int r = sl / PS::PIECES;
+      const int p = (sl % PS::PIECES) ^ swz<D>(r);
+      const int row = min(it.q0 + wave * 32 + r, it.C - 1);
+      lds_dma16((const uint8_t*)a.q + ((size_t)(it.qbeg + row) * a.Hq + it.h) * PS::ROWB + p * 16,
+                qb + wave * 32 * PS::ROWB + x * 1024);
+    }
   };
   auto live = [&](int j) __attribute__((always_inline)) { return wave_live && j * kPKT <= wave_last_pos; };
 
@@ -283,6 +442,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // queries.  The two accumulators alternate; the K fragments are read two
   // contraction steps ahead, in an order the scheduler may not sink.
   const int ksw = swz<D>(lq);  // rows lq and lq + 32 share it
+  const uint8_t* qrow = qb + (wave * 32 + lq) * PS::ROWB;  // this lane's query row
   auto s_phase = [&](auto r) __attribute__((always_inline)) {
     const uint8_t* k0 = kbuf(r) + lq * PS::ROWB;
     const uint8_t* k1 = k0 + 32 * PS::ROWB;
@@ -290,22 +450,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sacc[mt][rr] = 0.f;
-    uint4 f0[PS::KS], f1[PS::KS];
+    uint4 f0[PS::KS], f1[PS::KS], fq[PS::KS];
     auto kofs = [&](int ks) __attribute__((always_inline)) { return ((2 * ks + hh) ^ ksw) << 4; };
     f0[0] = *(const uint4*)(k0 + kofs(0));
     f1[0] = *(const uint4*)(k1 + kofs(0));
+    fq[0] = *(const uint4*)(qrow + kofs(0));
     f0[1] = *(const uint4*)(k0 + kofs(1));
     f1[1] = *(const uint4*)(k1 + kofs(1));
+    fq[1] = *(const uint4*)(qrow + kofs(1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < PS::KS; ++ks) {
       if (ks + 2 < PS::KS) {
         f0[ks + 2] = *(const uint4*)(k0 + kofs(ks + 2));
         f1[ks + 2] = *(const uint4*)(k1 + kofs(ks + 2));
+        fq[ks + 2] = *(const uint4*)(qrow + kofs(ks + 2));
       }
       __builtin_amdgcn_sched_barrier(0);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[ks]), qreg[ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1[ks]), qreg[ks], sacc[1], 0, 0, 0);
+      const bf16x8_t qf = __builtin_bit_cast(bf16x8_t, fq[ks]);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f0[ks]), qf, sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f1[ks]), qf, sacc[1], 0, 0, 0);
     }
   };
 
@@ -447,47 +611,100 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // other wavefronts at the barrier, after which tile j + 1 is whole.
   // Tile j + 2 goes over tile j - 1, which every wavefront finished before
   // the previous barrier.
-  auto step = [&](int j, auto r) __attribute__((always_inline)) {
-    constexpr int R = decltype(r)::value;
-    const bool more = j + 2 < n_tiles;
-    if (more) dma(j + 2, std::integral_constant<int, (R + 2) % 3>{});
-    if (live(j)) {
-      s_phase(r);
-      sm_phase(j);
-      o_phase(r);
+  // Output of item ci: the accumulated rows over their sums.
+  auto finish_item = [&]() __attribute__((always_inline)) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (row_ok) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = a.out + ((size_t)(ci.qbeg + my_row) * a.Hq + ci.h) * D;
+#pragma unroll
+      for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = dt * 32 + 8 * rq + 4 * hh;
+          const uint2 v = make_uint2(pack2_bf16(acc_o[dt][4 * rq] * inv, acc_o[dt][4 * rq + 1] * inv),
+                                     pack2_bf16(acc_o[dt][4 * rq + 2] * inv, acc_o[dt][4 * rq + 3] * inv));
+          *(uint2*)(op + d0) = v;
+        }
     }
-    if (more)
-      tile_barrier<2 * PS::DMA_PER_WAVE>();
-    else
-      tile_barrier<0>();
+#pragma unroll
+    for (int dt = 0; dt < PS::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
   };
 
-  dma(0, std::integral_constant<int, 0>{});
-  if (n_tiles > 1) {
-    dma(1, std::integral_constant<int, 1>{});
-    tile_barrier<2 * PS::DMA_PER_WAVE>();
-  } else {
-    tile_barrier<0>();
-  }
-  for (int j = 0; j < n_tiles; j += 3) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
-    if (j + 2 < n_tiles) step(j + 2, std::integral_constant<int, 2>{});
-  }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  const float inv = 1.f / l_tot;
-  uint16_t* op = a.out + ((size_t)(qbeg + my_row) * a.Hq + h) * D;
-#pragma unroll
-  for (int dt = 0; dt < PS::DT; ++dt)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = dt * 32 + 8 * rq + 4 * hh;
-      const uint2 v = make_uint2(pack2_bf16(acc_o[dt][4 * rq] * inv, acc_o[dt][4 * rq + 1] * inv),
-                                 pack2_bf16(acc_o[dt][4 * rq + 2] * inv, acc_o[dt][4 * rq + 3] * inv));
-      *(uint2*)(op + d0) = v;
+  // One step of the stream: transfer the tile two ahead (kept in buffer
+  // r + 2 mod 3, which held the tile computed two steps ago), compute tile
+  // tc of ci from buffer r, then wait for this wavefront's share of the
+  // next tile and meet the others at the barrier.  On the last tile of an
+  // item the next item's query rows go into LDS once this wavefront has
+  // read its own (after its S^T products); the barrier then waits for them
+  // too.  Returns false after the last item.
+  bool q_wait = false;  // the query rows of ci may still be on their way
+  auto step = [&](auto r) __attribute__((always_inline)) {
+    constexpr int R = decltype(r)::value;
+    constexpr int NT = 2 * PS::DMA_PER_WAVE;  // transfers of one tile per wavefront
+    const bool more = di.k >= 0;
+    if (more) dma_next(std::integral_constant<int, (R + 2) % 3>{});
+    if (q_wait) {
+      // the query rows went out before this step's tile transfers
+      if (more)
+        __builtin_amdgcn_s_waitcnt((NT & 15) | ((NT >> 4) << 14) | (7 << 4) | (15 << 8));
+      else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      q_wait = false;
     }
+    const bool last = tc == ci.n_tiles - 1;
+    const bool q_next = last && nci.k >= 0;
+    const bool lv = live(tc);
+    if (lv) s_phase(r);
+    if (q_next) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's query reads are done
+      q_dma(nci);
+    }
+    if (lv) {
+      sm_phase(tc);
+      o_phase(r);
+    }
+    if (q_next) {
+      if (more)
+        tile_barrier<NT + QX>();
+      else
+        tile_barrier<QX>();
+    } else if (more) {
+      tile_barrier<NT>();
+    } else {
+      tile_barrier<0>();
+    }
+    if (!last) {
+      ++tc;
+      return true;
+    }
+    finish_item();
+    ci = nci;
+    tc = 0;
+    if (ci.k < 0) return false;
+    nci = item_at(ci.k + 1);
+    set_rows();
+    q_wait = true;
+    return true;
+  };
+
+  // The first item's query rows, block ids and first two tiles are all in
+  // flight at once; the barrier waits for every one of them, so the
+  // compiler places no wait inside the loop.
+  q_dma(ci);
+  ent = entries();
+  dma_next(std::integral_constant<int, 0>{});
+  if (di.k >= 0) dma_next(std::integral_constant<int, 1>{});
+  tile_barrier<0>();
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if (!step(std::integral_constant<int, 2>{})) break;
+  }
 }
 
 bool prefill_supported(int dtype, int head_dim, int group, int block_size) {
@@ -519,10 +736,13 @@ int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total
   while ((1 << a.log2B) < B) ++a.log2B;
   a.q_tiles = (max_q_len + kPBM - 1) / kPBM;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const long long units = (long long)S * Hq;
-  const long long grid = (units + 7) / 8 * 8 * a.q_tiles;
-  if (grid <= 0) return 0;
-  if (grid > 0x7fffffffLL) return -2;
+  const long long items = (long long)S * Hq * a.q_tiles;
+  if (items <= 0) return 0;
+  if (items > 0x7fffffffLL) return -2;
+  const void* kfn = D == 128 ? (const void*)prefill_kernel<128> : (const void*)prefill_kernel<64>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kPThreads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const long long grid = std::min(items, (long long)per_cu * std::max(device_info().num_cus, 1));
   const dim3 g((unsigned)grid), b(kPThreads);
   if (D == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, g, b, 0, stream, a);
