@@ -226,10 +226,10 @@ def test_workspace_too_small_is_rejected():
 
 
 def test_workspace_reused_across_calls_and_garbage_filled():
-    """Split units are merged by the wavefront that arrives last; its arrival
-    counters live in the caller's workspace and carry a per-call epoch, so a
-    workspace reused by many calls, or filled with garbage, gives the same
-    results."""
+    """Partials and merge jobs live in the caller's workspace.  The main pass
+    writes every job entry before the merge reads it, and the merge reads only
+    partials written by the same call, so a workspace reused by calls of
+    different shapes, or filled with garbage, gives the same results."""
     wl_a = W.llama_decode(21, 24, 100, 3000, 8192, "llama-ws-a")
     wl_b = W.llama_decode(22, 40, 1, 2048, 8192, "llama-ws-b")
     st_a, st_b = driver.run_script(wl_a), driver.run_script(wl_b)

@@ -75,10 +75,22 @@ def test_prefill_empty_chunks_and_single_token():
     check(small("pf-empty", 77, [10, 0, 40, 0, 7], [5, 0, 33, 1, 0], 4, 2, 64, 16))
 
 
-def test_prefill_table_window_slides():
-    """Block size 1 and contexts past 1024 blocks: the workgroup's LDS window
-    of the block table has to slide while the key tiles advance."""
+def test_prefill_long_tables_block_size_1():
+    """Block size 1 (a block holds fewer keys than one 1 KiB transfer covers,
+    so every lane looks up its own block) and contexts past 1024 blocks."""
     check(small("pf-window", 91, [1100, 2500, 0], [50, 140, 1200], 4, 2, 64, 1))
+
+
+@pytest.mark.parametrize("n,hq,hkv,d", [(80, 8, 2, 128), (64, 4, 4, 64)])
+def test_prefill_many_items_per_workgroup(n, hq, hkv, d):
+    """More (sequence, head, q tile) items than workgroups, of mixed sizes
+    (one-tile items, empty second q tiles, prefixes 0..300): each workgroup
+    streams several items and the transfers run across item ends.  80
+    sequences take the batch order, 64 the ranked order."""
+    rng = np.random.default_rng(1000 + n)
+    prefix = [int(x) for x in rng.integers(0, 301, n)]
+    chunk = [int(x) for x in rng.integers(1, 301, n)]
+    check(small(f"pf-items-{n}", 95 + n, prefix, chunk, hq, hkv, d, 16))
 
 
 def test_prefill_opt13b_full():
