@@ -164,7 +164,7 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         from paged_kv_cache_364_amd import profiling
 
         tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE), [kname])
-        traffic = round(tb / 1e9, 4) if tb is not None else None
+        traffic = int(round(tb)) if tb is not None else None
         # matrix-core counters of the same kernel, if taken from these sources
         e = profiling.read_traffic(MFMA_FILE).get("kernels", {}).get(kname)
         if e is not None and e.get("sources_sha256") == profiling.sources_sha(e["group"]):
@@ -184,7 +184,8 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         "hbm_gbps_at_min_bytes": round((kv_bytes + qo_bytes) / (pf_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch"},
         "rocprof_mfma": mfma,
     }
     del kps, vps
@@ -540,7 +541,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "paged_attention_decode = decode_main + decode_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": round(tb / 1e9, 4) if tb is not None else None},
+                     "traffic": int(round(tb)) if tb is not None else None, "traffic_unit": "bytes per launch"},
     }
     got_decode = driver.out_to_f64(out)
     del kps, vps
