@@ -168,6 +168,13 @@ class BlockAllocator:
                 if lb >= have:
                     need += 1
                     have += 1
+            elif table[lb] < 0:
+                # a hole (a block released by a trim of the sequence this one
+                # was forked from) is a missing block: a write into it takes
+                # a fresh one, as a write past the table does
+                if lb not in seen_shared:
+                    seen_shared.add(lb)
+                    need += 1
             elif self.ref[table[lb]] > 1 and lb not in seen_shared:
                 seen_shared.add(lb)
                 need += 1
@@ -184,6 +191,10 @@ class BlockAllocator:
                 b = self._pop()
                 self.ref[b] = 1
                 table.append(b)
+            elif table[lb] < 0:
+                b = self._pop()
+                self.ref[b] = 1
+                table[lb] = b
             elif self.ref[table[lb]] > 1:
                 old = table[lb]
                 b = self._pop()
@@ -275,7 +286,9 @@ class BlockAllocator:
         if seq in self.swapped:
             raise AllocatorError(f"sequence {seq} is swapped out")
         tokens = [int(t) for t in tokens]
-        if not self.tok_ok[seq]:
+        B0, t0, l0 = self.block_size, self.tables[seq], self.lens[seq]
+        hole = l0 % B0 != 0 and len(t0) > l0 // B0 and t0[l0 // B0] < 0
+        if not self.tok_ok[seq] or hole:  # no hash chain, or a hole where the append starts
             slots, copies = self.append(seq, len(tokens))
             return slots, copies, 0
         B = self.block_size

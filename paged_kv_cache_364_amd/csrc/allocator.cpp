@@ -162,14 +162,22 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
   const int64_t start = s.len;
   const int64_t end = start + n;
   // Blocks needed: new logical blocks past the table, plus a copy of the
-  // partially filled last block if this append writes into it while shared.
+  // partially filled last block if this append writes into it while shared,
+  // or a fresh block if that entry is a hole (-1: released by a trim of the
+  // sequence this one was forked from; a write into a missing block takes a
+  // new one, as a write past the table does).
   const int64_t have = (int64_t)s.table.size();
   const int64_t want = (end + B - 1) / B;
   int64_t need = want > have ? want - have : 0;
   int copies = 0;
-  if (n > 0 && start / B < have && a->ref[(size_t)s.table[(size_t)(start / B)]] > 1) {
-    ++need;
-    copies = 1;
+  if (n > 0 && start / B < have) {
+    const int32_t b0 = s.table[(size_t)(start / B)];
+    if (b0 < 0) {
+      ++need;
+    } else if (a->ref[(size_t)b0] > 1) {
+      ++need;
+      copies = 1;
+    }
   }
   if (copies > 0 && (copy_cap < copies || !copy_pairs_out)) return PKV_ERR_INVALID;
   if (need > (int64_t)a->free_stack.size()) return PKV_ERR_NO_BLOCKS;
@@ -189,6 +197,10 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t
       const int32_t b = pop_block(a);
       a->ref[(size_t)b] = 1;
       s.table.push_back(b);
+    } else if (s.table[(size_t)lb] < 0) {
+      const int32_t b = pop_block(a);
+      a->ref[(size_t)b] = 1;
+      s.table[(size_t)lb] = b;
     } else if (a->ref[(size_t)s.table[(size_t)lb]] > 1) {
       const int32_t old = s.table[(size_t)lb];
       const int32_t b = pop_block(a);
@@ -213,7 +225,10 @@ int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int 
   if (it == a->seqs.end()) return PKV_ERR_INVALID;
   pkv_alloc::Seq& s = it->second;
   if (s.swapped) return PKV_ERR_STATE;
-  if (!s.tok_ok) {  // no hash chain (an earlier append carried no tokens): no caching
+  // no hash chain (an earlier append carried no tokens), or a hole where the
+  // append starts: no caching
+  if (!s.tok_ok || (s.len % a->block_size != 0 && (int64_t)s.table.size() > s.len / a->block_size &&
+                    s.table[(size_t)(s.len / a->block_size)] < 0)) {
     const int st = pkv_seq_append(a, seq, n, slots_out, copy_pairs_out, copy_cap, num_copies_out);
     if (st == PKV_OK && num_cached_out) *num_cached_out = 0;
     return st;

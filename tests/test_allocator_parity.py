@@ -245,6 +245,35 @@ def test_trim_then_fork_swap_and_free():
         a.trim(5, 0)
 
 
+def test_append_into_a_hole_takes_a_fresh_block():
+    """A fork inside a trimmed region leaves the child's partly filled last
+    block as a hole; the child's next write takes a fresh block there (no
+    copy), on both sides."""
+    a = BlockAllocator(16, 4)
+    o = OracleAlloc(16, 4)
+    for x in (a, o):
+        x.add(0)
+        x.append(0, 22)
+    assert a.trim(0, 12) == o.trim(0, 12) == 3
+    for x in (a, o):
+        x.fork(0, 1, 10)  # the child holds blocks 0..2, all holes; length 10 ends inside block 2
+    same_state(a, o)
+    assert a.table(1) == [-1, -1, -1]
+    s1, c1 = a.append(1, 3)
+    s2, c2 = o.append(1, 3)
+    assert s1.tolist() == s2 and c1 == c2 == []
+    t = a.table(1)
+    assert t[:2] == [-1, -1] and t[2] >= 0 and len(t) == 4
+    assert s2 == [t[2] * 4 + 2, t[2] * 4 + 3, t[3] * 4 + 0]
+    same_state(a, o)
+    for x in (a, o):
+        x.fork(0, 3, 10)
+    s1, c1, n1 = a.append_tokens(3, [1, 2, 3])
+    s2, c2, n2 = o.append_tokens(3, [1, 2, 3])
+    assert s1.tolist() == s2 and c1 == c2 == [] and n1 == n2 == 0
+    same_state(a, o)
+
+
 def test_swapped_sequence_refuses_append_and_fork():
     a = BlockAllocator(8, 4)
     a.add(0)
