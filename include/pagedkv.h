@@ -138,6 +138,11 @@ int pkv_swap_in(void* k_cache, void* v_cache, const int32_t* block_ids, int num,
  * Accumulation is fp32.  Long contexts are split across wavefronts; partial
  * results are merged with their log-sum-exp weights in a second kernel.
  * ---------------------------------------------------------------------- */
+/* Returns 0 for unsupported shapes.  The size depends on the decode grid:
+ * a fixed number of workgroups per compute unit, which the environment
+ * variable PKV_DECODE_WG_PER_CU (1..8) overrides.  Size the workspace with
+ * the same setting as the calls that use it; a call whose grid needs more
+ * than workspace_bytes returns PKV_ERR_WORKSPACE and launches nothing. */
 size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_blocks_per_seq, int dtype);
 
