@@ -118,7 +118,7 @@ def copy_bandwidth(torch, api, dev, mib=2048):
 
 
 def prefill_leg(args, torch, np, api, driver, workloads, dev):
-    wl = workloads.config5()
+    wl = workloads.opt13b_prefill_b16x512()
     st = driver.run_script(wl, device=dev)
     torch.cuda.synchronize()
     S, Hq, Hkv, D, B = len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
@@ -257,10 +257,10 @@ def prefix_cache_leg(torch, np, api, driver, workloads, dev, steps, warmup):
 
 
 def window_leg(torch, np, api, driver, workloads, dev, steps, warmup, window=512):
-    """Config 2's batch with a sliding window of `window` tokens: blocks
+    """The Llama-3.1-8B batch of 64 sequences with a sliding window of `window` tokens: blocks
     wholly before each window released (pkv_seq_trim), decode over the
     trimmed tables; GB/s over the K/V bytes the window holds."""
-    wl = workloads.config2()
+    wl = workloads.llama_decode_b64()
     st = driver.run_script(wl, device=dev)
     a = st.alloc
     used_before = a.stats().num_used
@@ -300,16 +300,16 @@ def unique_kv_tokens(np, tables, lens, B):
     return sum(held.values())
 
 
-def config_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4):
+def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4):
     """Decode on the other Llama-3.1-8B-shape batches: 256 log-normal
     contexts over a churned free list, and 32 prompts forked into 4 branches
     that share their prompt blocks.  Each rotates `layers` copies of its
     pools so that the working set exceeds the Infinity Cache."""
     res = {}
     stream = torch.cuda.current_stream()
-    for build, desc in ((workloads.config3, "256 contexts, log-normal (median 500, sigma 1, clip 1..8192), "
+    for build, desc in ((workloads.llama_ragged_b256, "256 contexts, log-normal (median 500, sigma 1, clip 1..8192), "
                                             "churned free list (seed 3)"),
-                        (workloads.config4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023}, "
+                        (workloads.llama_shared_prefix_32x4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023}, "
                                             "U{0..256} private tokens each (seed 4)")):
         wl = build()
         st = driver.run_script(wl, device=dev)
@@ -410,7 +410,7 @@ def main():
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the kernels have no "
+        print(json.dumps({"error": "pagedkv runs on one GPU only; --gpus must be 1 (the kernels have no "
                                    "multi-GPU path)"}))
         sys.exit(2)
 
@@ -429,7 +429,7 @@ def main():
                           f"layer, {max(1, args.layers)} layers rotated", "steps": args.steps}), flush=True)
         return
     t0 = time.time()
-    wl = workloads.config2()
+    wl = workloads.llama_decode_b64()
     log(f"workload {wl.name} generated in {time.time() - t0:.1f}s")
     st = driver.run_script(wl, device=dev)
     torch.cuda.synchronize()
@@ -560,7 +560,7 @@ def main():
     if not args.no_prefix_cache:
         result["prefix_cache"] = prefix_cache_leg(torch, np, api, driver, workloads, dev, 50, 5)
     if not args.no_configs:
-        result["other_batches"] = config_legs(torch, np, api, driver, workloads, dev, 50, 5)
+        result["other_batches"] = other_batch_legs(torch, np, api, driver, workloads, dev, 50, 5)
 
     pf = None
     if not args.no_prefill:

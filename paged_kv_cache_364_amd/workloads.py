@@ -220,7 +220,7 @@ LLAMA = dict(num_heads=32, num_kv_heads=8, head_dim=128)
 OPT13B = dict(num_heads=40, num_kv_heads=40, head_dim=128)
 
 
-def config1():
+def tiny_f32_decode():
     """Tiny fp32 decode: context lengths {10, 3, 17, 1}, 2 heads, head_dim 16,
     block size 4, 32-block pool in seeded random order, scale 1/sqrt(16)."""
     return decode_workload("tiny-f32-decode", 1, [10, 3, 17, 1], num_heads=2, num_kv_heads=2,
@@ -239,7 +239,7 @@ def llama_decode(seed=2, num_seqs=64, lo=128, hi=2048, num_blocks=25_600, name=N
     return wl
 
 
-def config2():
+def llama_decode_b64():
     return llama_decode(2, 64, 128, 2048, 25_600, "llama31-8b-decode-b64")
 
 
@@ -258,7 +258,7 @@ def ragged_decode(seed=3, num_seqs=256, num_blocks=25_600, churn_ops=2000, hi=81
                            churn_ops=churn_ops, max_blocks_per_seq=-(-hi // 16))
 
 
-def config3():
+def llama_ragged_b256():
     return ragged_decode(3, 256, 25_600, 2000, 8192, "llama31-8b-ragged-b256")
 
 
@@ -315,7 +315,7 @@ def shared_prefix(seed=4, num_prompts=32, prompt_len=1024, n_branches=4, fork_lo
                     max_blocks_per_seq=mb)
 
 
-def config4():
+def llama_shared_prefix_32x4():
     return shared_prefix(4, 32, 1024, 4, 1000, 1023, 256, 25_600, "llama31-8b-shared-prefix-32x4")
 
 
@@ -360,7 +360,7 @@ def prefill_workload(seed=5, num_seqs=16, prefix_hi=1536, chunk=512, num_blocks=
                     q_lens=cl, max_blocks_per_seq=max(mb, 1))
 
 
-def config5():
+def opt13b_prefill_b16x512():
     return prefill_workload(5, 16, 1536, 512, 4096, OPT13B, "opt13b-prefill-b16x512")
 
 
@@ -402,4 +402,6 @@ def shared_prompt_requests(seed=6, num_requests=16, prompt_len=1000, suffix_hi=2
                     steps=[a, b], batch=list(range(num_requests)), q=q, max_blocks_per_seq=mb)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# the five seeded workloads, by name
+WORKLOADS = {f.__name__: f for f in (tiny_f32_decode, llama_decode_b64, llama_ragged_b256, llama_shared_prefix_32x4,
+                                     opt13b_prefill_b16x512)}

@@ -58,8 +58,8 @@ def run_both(wl):
     same_state(a, o)
 
 
-def test_config1():
-    run_both(W.config1())
+def test_tiny_f32_decode_script():
+    run_both(W.tiny_f32_decode())
 
 
 def test_shrunk_workloads():
@@ -73,8 +73,8 @@ def test_shrunk_workloads():
 
 @pytest.mark.slow
 def test_full_workload_scripts():
-    for c in (2, 3, 4):
-        run_both(W.CONFIGS[c]())
+    for build in (W.llama_decode_b64, W.llama_ragged_b256, W.llama_shared_prefix_32x4):
+        run_both(build())
 
 
 def test_random_ops_match():

@@ -65,8 +65,8 @@ def check_workload(wl, pools_too=True):
     return st, ost, out
 
 
-def test_config1_tiny_fp32():
-    check_workload(W.config1())
+def test_tiny_f32_decode():
+    check_workload(W.tiny_f32_decode())
 
 
 VARIANTS = [
@@ -93,16 +93,16 @@ def test_llama_shape_small_pool_parity():
     check_workload(W.llama_decode(7, 16, 1, 700, 2048, "llama-small"))
 
 
-def test_config2_llama_decode_full():
-    check_workload(W.config2())
+def test_llama_decode_b64_full():
+    check_workload(W.llama_decode_b64())
 
 
-def test_config3_ragged_churn_full():
-    check_workload(W.config3())
+def test_llama_ragged_b256_full():
+    check_workload(W.llama_ragged_b256())
 
 
-def test_config4_shared_prefix_full():
-    st, ost, _ = check_workload(W.config4())
+def test_llama_shared_prefix_32x4_full():
+    st, ost, _ = check_workload(W.llama_shared_prefix_32x4())
     copies = sum(len(c) for c in st.step_copies)
     assert copies == sum(len(c) for c in ost.step_copies) > 0
 

@@ -95,7 +95,7 @@ def test_prefill_many_items_per_workgroup(n, hq, hkv, d):
 
 def test_prefill_opt13b_full():
     """16 sequences, prefix U{0..1536}, 512-token chunk, 40 heads, head_dim 128."""
-    check(W.config5())
+    check(W.opt13b_prefill_b16x512())
 
 
 def test_prefill_rows_match_decode():

@@ -354,8 +354,8 @@ def test_decode_vs_brute_force(G, B, dtype):
     check_decode_vs_brute_force(small_decode_workload(7 + G + B, G=G, B=B, dtype=dtype))
 
 
-def test_config1_vs_brute_force_and_blocks():
-    wl = W.config1()
+def test_tiny_f32_decode_vs_brute_force_and_blocks():
+    wl = W.tiny_f32_decode()
     st = runner.run(wl)
     assert list(st.context_lens) == [10, 3, 17, 1]
     assert st.alloc.num_blocks - st.alloc.num_free() == 10  # 3 + 1 + 5 + 1
