@@ -227,8 +227,10 @@ int pkv_seq_add(pkv_alloc* a, int64_t seq);
 /* Reserve slots for n new tokens.  slots_out: host int32 [n] (written).
  * copy_pairs_out: host int32 [copy_cap][2] receiving (src, dst) copies that
  * must be applied (pkv_copy_blocks) before the tokens are written; one append
- * produces at most one copy.  *num_copies_out gets the count.  Atomic: on
- * PKV_ERR_NO_BLOCKS or any error nothing changes. */
+ * produces at most one copy.  *num_copies_out gets the count.  A write into
+ * a -1 entry (a block released by pkv_seq_trim and shared as a hole by a
+ * fork) takes a fresh block there, as a write past the table does, with no
+ * copy.  Atomic: on PKV_ERR_NO_BLOCKS or any error nothing changes. */
 int pkv_seq_append(pkv_alloc* a, int64_t seq, int n, int32_t* slots_out, int32_t* copy_pairs_out,
                    int copy_cap, int* num_copies_out);
 
