@@ -300,7 +300,22 @@ def unique_kv_tokens(np, tables, lens, B):
     return sum(held.values())
 
 
-def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4):
+def calibration_copy(torch, api, dev, mib, Hkv=8, B=16, D=128):
+    """One copy_blocks launch of known size, for scaling HBM byte counters:
+    n source blocks -> n destination blocks of 64 KiB (K + V), so n * 64 KiB
+    are read and written."""
+    n = max(1, mib * 1024 * 1024 // (2 * Hkv * B * D * 2))
+    ck = torch.zeros((2 * n, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.zeros_like(ck)
+    pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], 1).to(torch.int32).to(dev).contiguous()
+    torch.cuda.synchronize()
+    api.copy_blocks(ck, cv, pairs)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {n} block pairs, {2 * n * Hkv * B * D * 2} bytes read and written")
+    del ck, cv
+
+
+def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, layers=4, only=None):
     """Decode on the other Llama-3.1-8B-shape batches: 256 log-normal
     contexts over a churned free list, and 32 prompts forked into 4 branches
     that share their prompt blocks.  Each rotates `layers` copies of its
@@ -311,6 +326,8 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
                                             "churned free list (seed 3)"),
                         (workloads.llama_shared_prefix_32x4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023}, "
                                             "U{0..256} private tokens each (seed 4)")):
+        if only is not None and build.__name__ != only:
+            continue
         wl = build()
         st = driver.run_script(wl, device=dev)
         torch.cuda.synchronize()
@@ -408,6 +425,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once with copy_blocks (a plain copy of known size, "
                          "for scaling HBM byte counters)")
+    ap.add_argument("--other-batch", choices=["llama_ragged_b256", "llama_shared_prefix_32x4"], default=None,
+                    help="instead of the benchmark, time the decode of this batch only (to profile it)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "pagedkv runs on one GPU only; --gpus must be 1 (the kernels have no "
@@ -421,6 +440,13 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.other_batch is not None:
+        if args.calibrate_copy_mib > 0:
+            calibration_copy(torch, api, dev, args.calibrate_copy_mib)
+        rows = other_batch_legs(torch, np, api, driver, workloads, dev, args.steps, args.warmup,
+                                only=args.other_batch)
+        print(json.dumps(rows), flush=True)
+        return
     if args.block_sweep is not None:
         sizes = args.block_sweep or [8, 16, 32, 64, 128, 256]
         args.block_sweep = sizes
@@ -458,16 +484,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.calibrate_copy_mib > 0:
-        # n source blocks -> n destination blocks of 64 KiB (K + V): n * 64 KiB read and written
-        n = max(1, args.calibrate_copy_mib * 1024 * 1024 // (2 * Hkv * B * D * 2))
-        ck = torch.zeros((2 * n, Hkv, B, D), dtype=q.dtype, device=dev)
-        cv = torch.zeros_like(ck)
-        pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], 1).to(torch.int32).to(dev).contiguous()
-        torch.cuda.synchronize()
-        api.copy_blocks(ck, cv, pairs)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {n} block pairs, {2 * n * Hkv * B * D * 2} bytes read and written")
-        del ck, cv
+        calibration_copy(torch, api, dev, args.calibrate_copy_mib)
 
     def decode(i):
         li = i % L

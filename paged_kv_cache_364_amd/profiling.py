@@ -7,9 +7,11 @@
 ``python -m paged_kv_cache_364_amd.profiling traffic FETCH_DIR WRITE_DIR CAL_BYTES OUT.txt CMD...``
     reads two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
     benchmark with ``--calibrate-copy-mib`` set, scales each counter by what
-    it reads for the calibration copy (the run's one copy_blocks dispatch,
-    which reads and writes CAL_BYTES bytes), and writes per-dispatch HBM bytes of every kernel of this
-    library, plus a JSON line that ``bench.py`` reads back.  The JSON carries
+    it reads for the calibration copy (the run's first copy_blocks dispatch,
+    which reads and writes CAL_BYTES bytes; later ones are copy-on-write
+    copies of the workload's setup and are left out), and writes per-dispatch
+    HBM bytes of every kernel of this library, plus a JSON line that
+    ``bench.py`` reads back.  The JSON carries
     the SHA-256 of the kernel sources, so a figure taken before a kernel
     changed is not reported for the new one.
 
@@ -87,12 +89,17 @@ def _pmc(d: str, counter: str) -> List[dict]:
 
 def traffic_summary(fetch_dir: str, write_dir: str, cal_bytes: int, out: str, cmd: str) -> Dict:
     fetch, write = _pmc(fetch_dir, "FETCH_SIZE"), _pmc(write_dir, "WRITE_SIZE")
-    # calibration: the one copy_blocks dispatch moves a known byte count; the
-    # benchmark prints it, and it is the only copy_blocks launch in the run
-    cal_f = [float(r["Counter_Value"]) for r in fetch if "copy_blocks" in r["Kernel_Name"]]
-    cal_w = [float(r["Counter_Value"]) for r in write if "copy_blocks" in r["Kernel_Name"]]
-    if len(cal_f) != 1 or len(cal_w) != 1:
-        raise RuntimeError("expected exactly one calibration copy_blocks dispatch per run")
+    # calibration: the run's first copy_blocks dispatch moves a known byte
+    # count (the benchmark issues it before any workload is set up)
+    def first_copy(rows):
+        c = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                   if "copy_blocks" in r["Kernel_Name"])
+        if not c:
+            raise RuntimeError("no calibration copy_blocks dispatch in the run")
+        return c[0][1]
+
+    cal_f = [first_copy(fetch)]
+    cal_w = [first_copy(write)]
     scale_f = cal_bytes / (cal_f[0] * KIB)
     scale_w = cal_bytes / (cal_w[0] * KIB)
     per: Dict[str, Dict[str, List[float]]] = {}

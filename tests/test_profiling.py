@@ -48,6 +48,18 @@ def test_traffic_summary_scales_by_calibration(tmp_path):
     assert profiling.traffic_bytes(back, ["missing"]) is None
 
 
+def test_traffic_calibration_is_the_first_copy(tmp_path):
+    """Later copy_blocks dispatches (copy-on-write copies of a workload's
+    setup) neither replace the calibration nor enter the table."""
+    fd, wd = str(tmp_path / "f"), str(tmp_path / "w")
+    cal = 1 << 20
+    write_pmc(fd, [(CB, "FETCH_SIZE", cal / 2048, 10), (CB, "FETCH_SIZE", 7.0, 10), (DM, "FETCH_SIZE", 50.0, 10)])
+    write_pmc(wd, [(CB, "WRITE_SIZE", cal / 1024, 10), (CB, "WRITE_SIZE", 7.0, 10), (DM, "WRITE_SIZE", 2.0, 10)])
+    r = profiling.traffic_summary(fd, wd, cal, str(tmp_path / "t.txt"), "cmd")
+    assert abs(r["scale_fetch"] - 2.0) < 1e-12 and abs(r["scale_write"] - 1.0) < 1e-12
+    assert list(r["kernels"]) == ["decode_main<bf16_t, 128, 4>"]
+
+
 def test_mfma_summary_medians(tmp_path):
     d = str(tmp_path / "m")
     write_pmc(d, [(PF, "MfmaUtil", 20.0, 300_000), (PF, "MfmaFlopsBF16", 1.9e11, 300_000),
