@@ -22,9 +22,11 @@
  *    physical block s / block_size at offset s % block_size.
  *  - Block tables are int32 [num_seqs][max_blocks_per_seq]; entry lb is the
  *    physical block of logical block lb (tokens lb*B .. lb*B+B-1).  Entries
- *    past ceil(context_len / block_size) are never read (pad them with -1).
- *    Table contents are trusted: an entry outside [0, num_blocks) is not
- *    dereferenced; rows that meet one produce NaN outputs.
+ *    past ceil(context_len / block_size) may be read but are never
+ *    dereferenced, and never change a result (pad them with -1).  Table
+ *    contents are trusted: an entry outside [0, num_blocks) is not
+ *    dereferenced; the output rows that attend a key of such a block are
+ *    NaN, and no other row changes.
  *  - Query head h reads KV head h / (num_heads / num_kv_heads).
  *  - Device pointers to element arrays must be 16-byte aligned
  *    (PKV_ERR_ALIGN otherwise); int32 arrays need 4-byte alignment.
@@ -175,8 +177,12 @@ int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_ca
  * and merging of partial results: intelliparadigm.com article, section 2.2.
  *
  *   out, q         device [total_q][num_heads][head_dim], bf16
- *   cu_q_lens      device int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing
- *   max_q_len      host bound on every C_s (sizes the launch)
+ *   cu_q_lens      device int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing,
+ *                  cu_q_lens[num_seqs] = total_q
+ *   max_q_len      host bound on every C_s (sizes the launch); >= 1 when
+ *                  total_q > 0 (PKV_ERR_INVALID otherwise).  Rows past
+ *                  ceil(max_q_len / 256) * 256 of a longer chunk are written
+ *                  as NaN, never left unwritten.
  *   context_lens   device int32 [num_seqs], each >= C_s
  * ---------------------------------------------------------------------- */
 int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q,

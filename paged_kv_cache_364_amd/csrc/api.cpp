@@ -213,7 +213,8 @@ int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_le
   // the prefill loads index pool rows (block, head, slot) in 32 bits
   if ((uint64_t)num_blocks * (uint64_t)num_kv_heads * (uint64_t)block_size > 0xffffffffull)
     return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PKV_OK;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (max_q_len == 0) return PKV_ERR_INVALID;  // total_q > 0: some chunk has a row
   if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
       !aligned4(context_lens) || !aligned4(cu_q_lens))

@@ -96,8 +96,10 @@ __device__ __forceinline__ int swz(int key) {
     return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
 }
 
-// Rows for keys with no data: zeros past the context, NaN for a block id
-// outside the pool (so the rows that attend it come out NaN).
+// Rows for keys with no data: zeros past the context; for a block id outside
+// the pool, a NaN key row and a zero value row, so exactly the query rows
+// that attend such a key come out NaN (a masked key's weight is 0, and
+// 0 times a zero value row stays 0).
 __device__ __attribute__((aligned(16))) uint16_t g_pf_zero_row[128];
 __device__ __attribute__((aligned(16))) uint16_t g_pf_nan_row[128] = {0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0, 0x7fc0};
 
@@ -182,9 +184,11 @@ __device__ __forceinline__ void dma_lanes(const PrefillArgs& a, const int32_t* t
       (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)kvh) << a.log2B) + (uint32_t)(t & ((1 << a.log2B) - 1));
   const size_t off = (size_t)row * D + p * 8;
   const bool real = in_ctx && !outside;
-  const uint16_t* fill = in_ctx ? g_pf_nan_row + p * 8 : g_pf_zero_row + p * 8;  // used when !real
-  const uint16_t* ksrc = real ? a.k_cache + off : fill;
-  const uint16_t* vsrc = real ? a.v_cache + off : fill;
+  // used when !real: a key of a block outside the pool scores NaN (its V is
+  // zero, so a row whose causal mask drops that key is unaffected)
+  const uint16_t* kfill = in_ctx ? g_pf_nan_row + p * 8 : g_pf_zero_row + p * 8;
+  const uint16_t* ksrc = real ? a.k_cache + off : kfill;
+  const uint16_t* vsrc = real ? a.v_cache + off : g_pf_zero_row + p * 8;
   lds_dma16(ksrc, kdst + g * 1024);
   lds_dma16(vsrc, vdst + g * 1024);
 }
@@ -228,8 +232,9 @@ __device__ __forceinline__ TileEntries<D> tile_entries(const PrefillArgs& a, con
 // When a block holds at least the 64 / PIECES keys of a transfer, the
 // transfer's block id (ent, read ahead through the scalar cache) gives the
 // block's address in SGPRs and the lanes add their fixed offsets (voff).
-// Keys past the context read the zero row and a block id outside the pool
-// reads the NaN row; those cases pick a source per lane.
+// Keys past the context read the zero row; a block id outside the pool
+// reads the NaN row for K and the zero row for V.  Those cases pick a source
+// per lane.
 template <int D>
 __device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int32_t* trow, const TileEntries<D>& ent,
                                          int kvh, int t0, int ctx, int wave, int lane, const uint32_t* voff,
@@ -261,10 +266,11 @@ __device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int32_t* tr
       const int key = sl / PS::PIECES;
       const int p = (sl % PS::PIECES) ^ swz<D>(key);
       const bool in_ctx = t0 + key < ctx;
-      const uint8_t* fill = (const uint8_t*)(in_ctx ? g_pf_nan_row : g_pf_zero_row) + p * 16;
+      const uint8_t* kfill = (const uint8_t*)(in_ctx ? g_pf_nan_row : g_pf_zero_row) + p * 16;
+      const uint8_t* vfill = (const uint8_t*)g_pf_zero_row + p * 16;
       const bool real = in_ctx && valid;
-      lds_dma16(real ? (const uint8_t*)a.k_cache + boff + voff[i] : fill, kdst + g * 1024);
-      lds_dma16(real ? (const uint8_t*)a.v_cache + boff + voff[i] : fill, vdst + g * 1024);
+      lds_dma16(real ? (const uint8_t*)a.k_cache + boff + voff[i] : kfill, kdst + g * 1024);
+      lds_dma16(real ? (const uint8_t*)a.v_cache + boff + voff[i] : vfill, vdst + g * 1024);
     }
   }
 }
@@ -613,6 +619,18 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // the previous barrier.
   // Output of item ci: the accumulated rows over their sums.
   auto finish_item = [&]() __attribute__((always_inline)) {
+    // Rows that no q tile of the launch covers (a chunk longer than the
+    // caller's bound on chunk lengths) come out NaN, never unwritten; the
+    // last q tile of the sequence writes them.
+    const int covered = a.q_tiles * kPBM;
+    if (ci.q0 + kPBM == covered && ci.C > covered) {
+      const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+      const int n = (ci.C - covered) * PS::PIECES;
+      for (int i = tid; i < n; i += kPThreads) {
+        const int r = covered + i / PS::PIECES;
+        *(uint4*)(a.out + ((size_t)(ci.qbeg + r) * a.Hq + ci.h) * D + (i % PS::PIECES) * 8) = nan8;
+      }
+    }
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (row_ok) {
       const float inv = 1.f / l_tot;

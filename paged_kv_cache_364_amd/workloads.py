@@ -268,14 +268,21 @@ PROMPT_SEQ_BASE = 10_000
 def shared_prefix(seed=4, num_prompts=32, prompt_len=1024, n_branches=4, fork_lo=1000,
                   fork_hi=1023, priv_hi=256, num_blocks=25_600, name=None, fork_points=None):
     """Parallel sampling: each prompt is forked into ``n_branches`` branches at
-    a point f ~ U{fork_lo..fork_hi}; the prompt is then released, so the
+    a point f drawn uniformly from fork_lo..fork_hi minus the multiples of the
+    block size; the prompt is then released, so the
     branches hold the shared blocks alone.  Each branch writes p ~ U{0..priv_hi}
     private tokens, then one decode token (context f + p + 1)."""
     rng = np.random.default_rng(seed)
     bsz = 16
     hkv, d = LLAMA["num_kv_heads"], LLAMA["head_dim"]
     if fork_points is None:
-        forks = rng.integers(fork_lo, fork_hi + 1, size=num_prompts)
+        # uniform over the fork points inside a block, so that every branch's
+        # first write lands in a shared, partly filled block and forces a
+        # copy (block-aligned forks are exercised with explicit fork_points)
+        cands = np.array([f for f in range(fork_lo, fork_hi + 1) if f % bsz], dtype=np.int64)
+        if len(cands) == 0:
+            cands = np.arange(fork_lo, fork_hi + 1, dtype=np.int64)
+        forks = cands[rng.integers(0, len(cands), size=num_prompts)]
     else:
         forks = np.asarray(fork_points, dtype=np.int64)
         assert len(forks) == num_prompts

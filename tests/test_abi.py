@@ -23,6 +23,68 @@ def test_header_matches_binding():
     assert set(declared_functions()) == set(N.SIGNATURES)
 
 
+def declared_parameters():
+    """name -> list of C parameter types, parsed from the header."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(pkv_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = " ".join(m.group(2).split())
+        if params in ("", "void"):
+            out[m.group(1)] = []
+            continue
+        types = []
+        for p in params.split(","):
+            p = p.strip()
+            if "*" in p:
+                types.append("ptr")
+            else:
+                types.append(" ".join(p.split()[:-1]).replace("const ", ""))
+        out[m.group(1)] = types
+    return out
+
+
+C_TO_CTYPES = {"int": ctypes.c_int, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t,
+               "float": ctypes.c_float}
+
+
+def test_binding_argument_lists_match_header():
+    """Every binding passes as many arguments as the header declares, each
+    of the declared kind (pointer, int, int64_t, size_t, float), so no call
+    can shift an argument into the wrong slot."""
+    decl = declared_parameters()
+    assert set(decl) == set(N.SIGNATURES)
+    for name, types in decl.items():
+        argtypes = N.SIGNATURES[name][1]
+        assert len(argtypes) == len(types), (name, len(argtypes), len(types))
+        for i, (ct, at) in enumerate(zip(types, argtypes)):
+            if ct == "ptr":
+                assert at is ctypes.c_void_p or issubclass(at, ctypes._Pointer), (name, i, at)
+            else:
+                assert at is C_TO_CTYPES[ct], (name, i, ct, at)
+
+
+def test_boundary_argument_orders():
+    """The orders that differ from a plain reading of the problem statement
+    are pinned here (and listed with their reasons in the design notes):
+    cache geometry is (num_blocks, num_kv_heads, block_size, head_dim), the
+    order of the cache layout's own dimensions."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+
+    def names(fn):
+        m = re.search(r"\b" + fn + r"\s*\(([^)]*)\)\s*;", text)
+        return [re.split(r"[\s*]+", p.strip())[-1] for p in m.group(1).split(",")]
+    for fn in ("pkv_kv_write", "pkv_copy_blocks", "pkv_swap_out", "pkv_swap_in"):
+        n = names(fn)
+        i = n.index("num_blocks")
+        assert n[i: i + 4] == ["num_blocks", "num_kv_heads", "block_size", "head_dim"], fn
+    n = names("pkv_paged_attention_decode")
+    assert n[:7] == ["out", "q", "k_cache", "v_cache", "block_tables", "max_blocks_per_seq", "context_lens"]
+    assert n[-4:] == ["dtype", "workspace", "workspace_bytes", "stream"]
+    n = names("pkv_paged_attention_prefill")
+    assert n[:5] == ["out", "q", "cu_q_lens", "total_q", "max_q_len"]
+
+
 def test_library_exports_every_symbol():
     L = N.lib()
     for name in declared_functions():

@@ -158,3 +158,51 @@ def test_prefill_ignores_table_padding():
     api.paged_attention_prefill(out, q, cu, max(wl.q_lens), st.k_pool, st.v_pool, tb, st.lens_dev, scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_prefill_out_of_range_block_after_some_rows():
+    """A block outside the pool that only the later rows of a chunk reach:
+    the rows before it match the oracle (the bad keys are masked for them,
+    and a masked key's value row must not leak NaN), the rows from it on
+    are NaN."""
+    wl = small("pf-badblock-mid", 82, [0, 24], [40, 20], 4, 4, 128, 16)
+    st = driver.run_script(wl)
+    ost = oracle_runner.run(wl)
+    exp = oracle_runner.expected(wl, ost)
+    tb = st.tables_dev.clone()
+    tb[0, 1] = 1 << 30  # keys 16..31 of sequence 0 unreachable
+    q = driver.to_device(wl.q, "bf16", "cuda")
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(driver.cu_lens(wl.q_lens)).cuda()
+    say("[gpu] pf-badblock-mid: prefill")
+    api.paged_attention_prefill(out, q, cu, max(wl.q_lens), st.k_pool, st.v_pool, tb, st.lens_dev,
+                                float(wl.scale))
+    torch.cuda.synchronize()
+    got = driver.out_to_f64(out)
+    # sequence 0 (prefix 0): rows 0..15 never attend keys 16..31
+    assert np.isfinite(got[:16]).all()
+    assert float(np.abs(got[:16] - exp[:16]).max()) <= BF16_TOL
+    assert np.isnan(got[16:40]).all()
+    # sequence 1 is untouched
+    assert float(np.abs(got[40:] - exp[40:]).max()) <= BF16_TOL
+
+
+def test_prefill_chunk_longer_than_max_q_len_gives_nan_rows():
+    """max_q_len smaller than a chunk: the launch covers 256-row q tiles up
+    to max_q_len; rows of a longer chunk past that come out NaN, every other
+    row matches the oracle."""
+    wl = small("pf-overflow", 83, [10, 3], [300, 40], 4, 2, 128, 16)
+    st = driver.run_script(wl)
+    ost = oracle_runner.run(wl)
+    exp = oracle_runner.expected(wl, ost)
+    q = driver.to_device(wl.q, "bf16", "cuda")
+    out = torch.zeros_like(q)
+    cu = torch.from_numpy(driver.cu_lens(wl.q_lens)).cuda()
+    say("[gpu] pf-overflow: prefill with max_q_len 200")
+    api.paged_attention_prefill(out, q, cu, 200, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev,
+                                float(wl.scale))
+    torch.cuda.synchronize()
+    got = driver.out_to_f64(out)
+    assert float(np.abs(got[:256] - exp[:256]).max()) <= BF16_TOL
+    assert np.isnan(got[256:300]).all()
+    assert float(np.abs(got[300:] - exp[300:]).max()) <= BF16_TOL

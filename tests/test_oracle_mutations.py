@@ -224,3 +224,26 @@ def test_window_off_by_one_is_caught(monkeypatch):
 
     monkeypatch.setattr(attention, "decode", wider)
     assert fails(P.check_window_decode)
+
+
+def _to_f64_with(shift=16, as_fp16=False):
+    real = attention.to_f64
+
+    def to_f64(raw, dtype):
+        if dtype != "bf16":
+            return real(raw, dtype)
+        u = np.asarray(raw, dtype=np.uint16)
+        if as_fp16:
+            return u.view(np.float16).astype(np.float64)
+        return (u.astype(np.uint32) << np.uint32(shift)).view(np.float32).astype(np.float64)
+    return to_f64
+
+
+def test_bf16_shift_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(attention, "to_f64", _to_f64_with(shift=15))
+    assert fails(P.check_bf16_decoding)
+
+
+def test_bf16_read_as_fp16_is_caught(monkeypatch):
+    monkeypatch.setattr(attention, "to_f64", _to_f64_with(as_fp16=True))
+    assert fails(P.check_bf16_decoding)

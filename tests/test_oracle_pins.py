@@ -48,6 +48,65 @@ def test_bf16_rounding_matches_torch():
 
 
 # ---------------------------------------------------------------------------
+# oracle: decoding of stored bf16 bits (every bf16 attention value goes
+# through attention.to_f64).  bfloat16 is the upper half of an IEEE-754
+# binary32: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.  The
+# expected values below are decoded by hand from that definition, and the
+# random cross-check decodes each field with math.ldexp, not with a shift.
+# ---------------------------------------------------------------------------
+BF16_HAND = [
+    (0x3F80, 1.0),
+    (0xC040, -3.0),
+    (0xC000, -2.0),
+    (0x4049, 3.140625),          # 2 * (1 + 73/128)
+    (0x3E80, 0.25),
+    (0x0080, 2.0 ** -126),       # smallest normal
+    (0x0001, 2.0 ** -133),       # smallest subnormal: 2^-126 * 2^-7
+    (0x007F, 127 * 2.0 ** -133),  # largest subnormal
+    (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127),  # largest finite
+    (0x7F80, math.inf),
+    (0xFF80, -math.inf),
+]
+
+
+def bf16_by_fields(bits: int) -> float:
+    """Value of a bf16 bit pattern from its sign, exponent and fraction."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return math.nan if f else sign * math.inf
+    if e == 0:
+        return sign * math.ldexp(f, -133)
+    return sign * math.ldexp(128 + f, e - 134)
+
+
+def check_bf16_decoding():
+    bits = np.array([b for b, _ in BF16_HAND], dtype=np.uint16)
+    got = attention.to_f64(bits, "bf16")
+    assert got.dtype == np.float64
+    assert [float(x) for x in got] == [v for _, v in BF16_HAND]
+    # signed zeros and NaNs
+    z = attention.to_f64(np.array([0x0000, 0x8000], dtype=np.uint16), "bf16")
+    assert z[0] == 0.0 and not math.copysign(1.0, z[0]) < 0
+    assert z[1] == 0.0 and math.copysign(1.0, z[1]) < 0
+    assert np.isnan(attention.to_f64(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16), "bf16")).all()
+    # shape is kept; every finite pattern of a seeded draw decodes field by field
+    rng = np.random.default_rng(7)
+    r = rng.integers(0, 1 << 16, size=(3, 5, 64), dtype=np.uint16)
+    got = attention.to_f64(r, "bf16")
+    assert got.shape == r.shape
+    exp = np.array([bf16_by_fields(int(b)) for b in r.ravel()]).reshape(r.shape)
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    fin = ~np.isnan(exp)
+    assert np.array_equal(got[fin], exp[fin])
+
+
+def test_bf16_decoding_hand_bits():
+    check_bf16_decoding()
+
+
+# ---------------------------------------------------------------------------
 # allocator
 # ---------------------------------------------------------------------------
 def check_worked_example_b4():
@@ -503,6 +562,19 @@ def test_shared_prefix_copy_counts():
     a = st.alloc
     for s in wl.batch:
         assert len(a.table(s)) == -(-a.length(s) // 16)
+
+
+def test_shared_prefix_full_config_forces_copies():
+    """The full shared-prefix batch: every fork lies inside a block, so each
+    prompt's shared partial block is copied by three of its four branches
+    (the last holder writes in place) before their first write."""
+    wl = W.llama_shared_prefix_32x4()
+    forks = [op.fork_pos for st in wl.steps for op in st.ops if op.kind == "fork"]
+    assert len(forks) == 128 and all(f % 16 for f in forks)
+    assert all(1000 <= f <= 1023 for f in forks)
+    st = runner.run(wl, with_pools=False)
+    copies = [c for cs in st.step_copies for c in cs]
+    assert len(copies) == 3 * 32
 
 
 def test_ragged_lengths_and_churn():
