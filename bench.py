@@ -152,7 +152,8 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         li = i % L
         api.kv_write(kn, vn, slots, kps[li], vps[li])
 
-    pf_ms, pf_all = timed_calls(torch, prefill, args.prefill_steps, args.warmup, stream)
+    # the matrix cores' clocks take a few tens of calls to settle
+    pf_ms, pf_all = timed_calls(torch, prefill, args.prefill_steps, max(args.warmup, 40), stream)
     kw_ms, _ = timed_calls(torch, write, args.prefill_steps, args.warmup, stream)
     tflops = flops / (pf_ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
@@ -236,7 +237,7 @@ def prefix_cache_leg(torch, np, api, driver, workloads, dev, steps, warmup):
         st = driver.run_script(wl, device=dev)
         q = driver.to_device(wl.q, wl.dtype, dev)
         out = torch.empty_like(q)
-        ws = torch.empty(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
+        ws = torch.zeros(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
                                                    wl.block_size, wl.max_blocks_per_seq, q.dtype),
                          dtype=torch.uint8, device=dev)
 
@@ -269,7 +270,7 @@ def window_leg(torch, np, api, driver, workloads, dev, steps, warmup, window=512
     tables_dev, lens_dev = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
     q = driver.to_device(wl.q, wl.dtype, dev)
     out = torch.empty_like(q)
-    ws = torch.empty(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
+    ws = torch.zeros(api.decode_workspace_size(len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim,
                                                wl.block_size, wl.max_blocks_per_seq, q.dtype),
                      dtype=torch.uint8, device=dev)
 
@@ -341,7 +342,7 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
             vps.append(st.v_pool.clone())
         q = driver.to_device(wl.q, wl.dtype, dev)
         out = torch.empty_like(q)
-        ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+        ws = torch.zeros(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
                          dtype=torch.uint8, device=dev)
 
         def decode(i):
@@ -360,6 +361,52 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
         res[wl.name] = r
         del st, kps, vps, q, out, ws
         torch.cuda.empty_cache()
+    return res
+
+
+def gather_ceiling_leg(torch, np, api, kps, vps, tables, lens, B, steps, warmup):
+    """Bandwidth ceiling of the paged access pattern on this device: the
+    same pools, rotated the same way, read by a kernel that only loads
+    (pkv_gather_units).  Three unit lists:
+      - decode_units: the (block, kv head) slices the decode reads, K and V,
+        from the batch's own tables (4 KiB each at the Llama shape);
+      - random_4k: as many random 4 KiB (block, kv head) slices;
+      - random_32k: random whole blocks (all kv heads, 32 KiB per tensor),
+        the same bytes in 8x longer contiguous runs.
+    GB/s counts the bytes the units hold."""
+    Nb, Hkv, Bb, D = kps[0].shape
+    slice_kib = Bb * D * kps[0].element_size() // 1024
+    blk_kib = Hkv * slice_kib
+    rng = np.random.default_rng(12)
+    units = []
+    for t, n in zip(tables, lens):
+        for lb in range((int(n) + B - 1) // B):
+            b = int(t[lb])
+            units.extend(b * Hkv + h for h in range(Hkv))
+    n4 = len(units)
+    lists = {
+        "decode_units": (np.array(units, dtype=np.int32), slice_kib),
+        "random_4k": (rng.choice(Nb * Hkv, size=n4, replace=False).astype(np.int32), slice_kib),
+        "random_32k": (rng.choice(Nb, size=max(1, n4 // Hkv), replace=False).astype(np.int32), blk_kib),
+    }
+    sink = torch.zeros(8192, dtype=torch.int32, device=kps[0].device)
+    stream = torch.cuda.current_stream()
+    L = len(kps)
+    res = {}
+    for name, (ids, kib) in lists.items():
+        idt = torch.from_numpy(ids).to(kps[0].device)
+        nbytes = 2 * len(ids) * kib * 1024
+
+        def read(i):
+            api.gather_units(kps[i % L], vps[i % L], idt, kib, sink)
+
+        ms, _ = timed_calls(torch, read, steps, warmup, stream, per_call=False)
+        res[name] = {"unit_kib": kib, "units_per_pool": int(len(ids)), "bytes": nbytes,
+                     "us_avg": round(ms * 1e3, 2), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        log(f"gather {name}: {res[name]}")
+    res["note"] = ("read-only kernel over the decode's own pools, layers rotated as for the decode; K and V "
+                   "units both read")
     return res
 
 
@@ -384,7 +431,7 @@ def block_sweep(args, torch, np, api, driver, workloads, dev):
             vps.append(st.v_pool.clone())
         q = driver.to_device(wl.q, wl.dtype, dev)
         out = torch.empty_like(q)
-        ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+        ws = torch.zeros(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
                          dtype=torch.uint8, device=dev)
 
         def decode(i):
@@ -418,6 +465,8 @@ def main():
     ap.add_argument("--no-prefix-cache", action="store_true")
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the ragged and shared-prefix decode batches")
+    ap.add_argument("--no-gather-ceiling", action="store_true")
+    ap.add_argument("--no-block-sweep", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-sweep", type=int, nargs="*", default=None,
@@ -478,7 +527,7 @@ def main():
     kn = driver.to_device(np.concatenate([op.k for op in dec.ops]), wl.dtype, dev)
     vn = driver.to_device(np.concatenate([op.v for op in dec.ops]), wl.dtype, dev)
     slots = torch.tensor(st.step_slots[-1], dtype=torch.int32, device=dev)
-    ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+    ws = torch.zeros(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
                      dtype=torch.uint8, device=dev)
     scale = float(wl.scale)
     stream = torch.cuda.current_stream()
@@ -560,6 +609,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": int(round(tb)) if tb is not None else None, "traffic_unit": "bytes per launch"},
     }
+    if not args.no_gather_ceiling:
+        gc = gather_ceiling_leg(torch, np, api, kps, vps, st.tables, st.context_lens, B, 100, 10)
+        result["gather_ceiling"] = gc
+        result["roofline"]["frac_of_gather_ceiling"] = round(achieved / gc["decode_units"]["gbps"], 4)
     got_decode = driver.out_to_f64(out)
     del kps, vps
     torch.cuda.empty_cache()
@@ -578,6 +631,17 @@ def main():
         result["prefix_cache"] = prefix_cache_leg(torch, np, api, driver, workloads, dev, 50, 5)
     if not args.no_configs:
         result["other_batches"] = other_batch_legs(torch, np, api, driver, workloads, dev, 50, 5)
+
+    if not args.no_block_sweep:
+        class SweepArgs:
+            block_sweep = [8, 16, 32, 64, 128, 256]
+            layers = 8
+            steps = 50
+            warmup = 5
+        rows = block_sweep(SweepArgs, torch, np, api, driver, workloads, dev)
+        result["block_sweep"] = {"rows": rows, "workload": "llama31-8b-decode-b64 lengths and values (seed 2), "
+                                 "409,600-token pool per layer, 8 layers rotated, decode only",
+                                 "steps": SweepArgs.steps}
 
     pf = None
     if not args.no_prefill:

@@ -136,7 +136,8 @@ int pkv_swap_in(void* k_cache, void* v_cache, const int32_t* block_ids, int num,
  *                  step wrote.  <= 0 gives zeros; values above
  *                  max_blocks_per_seq * block_size are clamped to it.
  *   workspace      device scratch of at least pkv_decode_workspace_size(...)
- *                  bytes, private to this call until it completes on `stream`
+ *                  bytes, private to this call until it completes on `stream`;
+ *                  its contents need no initialisation
  * Accumulation is fp32.  Long contexts are split across wavefronts; partial
  * results are merged with their log-sum-exp weights in a second kernel.
  * ---------------------------------------------------------------------- */
@@ -191,6 +192,24 @@ int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_le
                                 const int32_t* context_lens, int num_seqs, int num_heads,
                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                 float scale, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gather_units: a measurement aid, not part of the attention path.  Reads
+ * every listed unit once and computes nothing else, so its rate is the HBM
+ * bandwidth ceiling of the paged access pattern (a table lookup, then a
+ * contiguous run per block; "08. PagedAttention", section "block size":
+ * smaller blocks mean more scattered reads).
+ *
+ *   pool_a, pool_b   device pools of pool_units units of unit_kib KiB each
+ *                    (pool_b may be NULL; when given, unit i is read from both)
+ *   unit_ids         device int32 [num_units]: units to read; ids outside
+ *                    [0, pool_units) are skipped
+ *   unit_kib         a power of two from 1 to 4096
+ *   sink             device uint32 [sink_words], sink_words >= 4: one folded
+ *                    word per wavefront (keeps the loads live; no meaning)
+ * ---------------------------------------------------------------------- */
+int pkv_gather_units(const void* pool_a, const void* pool_b, const int32_t* unit_ids, int num_units, int unit_kib,
+                     int64_t pool_units, void* sink, int sink_words, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host block allocator: builds block tables, slot mappings and copy lists.

@@ -62,6 +62,7 @@ SIGNATURES = {
                                                   c_int, c_int, c_float, c_int, vp, c_size, vp]),
     "pkv_paged_attention_prefill": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp, c_int, vp, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_float, c_int, vp]),
+    "pkv_gather_units": (c_int, [vp, vp, vp, c_int, c_int, c_i64, vp, c_int, vp]),
     "pkv_alloc_create": (vp, [c_int, c_int, i32p]),
     "pkv_alloc_destroy": (None, [vp]),
     "pkv_seq_add": (c_int, [vp, c_i64]),

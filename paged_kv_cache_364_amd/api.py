@@ -129,7 +129,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     mb = block_tables.shape[1]
     if workspace is None:
-        workspace = torch.empty(decode_workspace_size(S, Hq, H, D, B, mb, q.dtype), dtype=torch.uint8,
+        workspace = torch.zeros(decode_workspace_size(S, Hq, H, D, B, mb, q.dtype), dtype=torch.uint8,
                                 device=q.device)
     args = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), mb, _dev(context_lens, "context_lens", torch.int32), S,
@@ -141,6 +141,21 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     else:
         N.check(N.lib().pkv_paged_attention_decode(*args, *tail), "paged_attention_decode")
     return out
+
+
+def gather_units(pool_a: torch.Tensor, pool_b: Optional[torch.Tensor], unit_ids: torch.Tensor, unit_kib: int,
+                 sink: torch.Tensor, stream=None) -> None:
+    """Read every listed unit of unit_kib KiB of pool_a (and pool_b) once,
+    with no other arithmetic (pkv_gather_units): the bandwidth ceiling of the
+    paged access pattern.  sink: int32 GPU tensor, one word per wavefront."""
+    nbytes = pool_a.numel() * pool_a.element_size()
+    if pool_b is not None and pool_b.numel() * pool_b.element_size() != nbytes:
+        raise ValueError("pool_a and pool_b must have the same size")
+    pool_units = nbytes // (int(unit_kib) * 1024)
+    N.check(N.lib().pkv_gather_units(
+        _dev(pool_a, "pool_a"), _dev(pool_b, "pool_b") if pool_b is not None else None,
+        _dev(unit_ids, "unit_ids", torch.int32), unit_ids.numel(), int(unit_kib), pool_units,
+        _dev(sink, "sink", torch.int32), sink.numel(), _stream(stream)), "gather_units")
 
 
 def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,

@@ -198,6 +198,18 @@ int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_ca
                      workspace_bytes, stream);
 }
 
+int pkv_gather_units(const void* pool_a, const void* pool_b, const int32_t* unit_ids, int num_units, int unit_kib,
+                     int64_t pool_units, void* sink, int sink_words, void* stream) {
+  if (num_units < 0 || pool_units <= 0 || sink_words < 4) return PKV_ERR_INVALID;
+  if (!pow2(unit_kib) || unit_kib > 4096) return PKV_ERR_UNSUPPORTED;
+  if (num_units == 0) return PKV_OK;
+  if (!pool_a || !unit_ids || !sink) return PKV_ERR_INVALID;
+  if (!aligned16(pool_a) || (pool_b && !aligned16(pool_b)) || !aligned4(unit_ids) || !aligned4(sink))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_gather_units(pool_a, pool_b, unit_ids, num_units, unit_kib, (long long)pool_units, sink,
+                                  sink_words, (hipStream_t)stream);
+}
+
 int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
                                 const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 int max_blocks_per_seq, const int32_t* context_lens, int num_seqs, int num_heads,

@@ -25,8 +25,8 @@
 // the boundary between two (kv head, sequence) units, whose block-table
 // window and query rows are fetched as soon as the previous unit starts.
 //
-// Inside a chunk.  Lanes load the K and V rows with coalesced 16-byte loads
-// straight into registers: lane l holds 16 bytes (piece l % LR) of row
+// Inside a chunk.  Lanes load the K and V rows with coalesced 16-byte
+// non-temporal loads straight into registers: lane l holds 16 bytes (piece l % LR) of row
 // (l / LR) + j * RW for j < J.  All G query heads of the KV head share those
 // registers (grouped-query attention, cnblogs section 6).  QK^T partial sums
 // are finished by a DPP transpose-reduce inside each row group, leaving each
@@ -38,6 +38,15 @@
 #include "kernels.h"
 
 namespace pkv {
+
+// 16-byte load that does not keep the line in the caches: each K/V byte of
+// a decode step is read once, so there is nothing to gain by caching it,
+// and streaming past the caches reads faster on this chip.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 struct DecodeArgs {
   void* out;
@@ -257,8 +266,8 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       const unsigned off = loff + (unsigned)(j * SH::RW * D * SH::ES);
       const bool in = t0 + r >= u.lo && t0 + r < u.ctx;
       if (bok && (full || in)) {
-        ch.k[j] = *(const uint4*)(kp + off);
-        ch.v[j] = *(const uint4*)(vp + off);
+        ch.k[j] = load_stream(kp + off);
+        ch.v[j] = load_stream(vp + off);
         ch.ok |= 1 << j;
       } else {
         ch.k[j] = make_uint4(0, 0, 0, 0);
@@ -279,8 +288,8 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       if (t >= u.lo && t < u.ctx) {
         if ((unsigned)blk < (unsigned)a.num_blocks) {
           const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + cl * 16;
-          ch.k[j] = *(const uint4*)(u.kb + off);
-          ch.v[j] = *(const uint4*)(u.vb + off);
+          ch.k[j] = load_stream(u.kb + off);
+          ch.v[j] = load_stream(u.vb + off);
           ch.ok |= 1 << j;
         } else {
           ch.bad |= 1 << j;

@@ -32,6 +32,9 @@ int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n
 int launch_swap_blocks(bool out, void* k_cache, void* v_cache, const int32_t* ids, int n, int num_blocks, int Hkv,
                        int B, int D, int elem_bytes, void* host_k, void* host_v, hipStream_t stream);
 
+int launch_gather_units(const void* pool_a, const void* pool_b, const int32_t* ids, int n_units, int unit_kib,
+                        long long pool_units, void* sink, int sink_words, hipStream_t stream);
+
 bool decode_supported(int dtype, int head_dim, int group);
 size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_blocks, int B);
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,

@@ -169,3 +169,16 @@ def test_prefill_rejects_bad_arguments():
                                          None) == N.PKV_ERR_UNSUPPORTED
     assert L.pkv_paged_attention_prefill(p, p, p, 0, 0, p, p, p, 4, p, 2, 8, 8, 128, 16, (1 << 25) - 1, 0.1, 1,
                                          None) == N.PKV_OK
+
+
+def test_gather_units_rejects_bad_arguments():
+    L = N.lib()
+    p = fake()
+    assert L.pkv_gather_units(p, p, p, 4, 3, 64, p, 16, None) == N.PKV_ERR_UNSUPPORTED   # 3 KiB units
+    assert L.pkv_gather_units(p, p, p, 4, 8192, 64, p, 16, None) == N.PKV_ERR_UNSUPPORTED
+    assert L.pkv_gather_units(p, p, p, -1, 4, 64, p, 16, None) == N.PKV_ERR_INVALID
+    assert L.pkv_gather_units(p, p, p, 4, 4, 0, p, 16, None) == N.PKV_ERR_INVALID
+    assert L.pkv_gather_units(p, p, p, 4, 4, 64, p, 2, None) == N.PKV_ERR_INVALID       # sink too small
+    assert L.pkv_gather_units(None, p, p, 4, 4, 64, p, 16, None) == N.PKV_ERR_INVALID
+    assert L.pkv_gather_units(fake(0x100004), None, p, 4, 4, 64, p, 16, None) == N.PKV_ERR_ALIGN
+    assert L.pkv_gather_units(p, None, p, 0, 4, 64, p, 16, None) == N.PKV_OK

@@ -34,7 +34,7 @@ def test_decode_step_graph_replays_match_eager():
     kn = driver.to_device(np.concatenate([op.k for op in dec.ops]), wl.dtype, "cuda")
     vn = driver.to_device(np.concatenate([op.v for op in dec.ops]), wl.dtype, "cuda")
     slots = torch.tensor(st.step_slots[-1], dtype=torch.int32, device="cuda")
-    ws = torch.empty(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+    ws = torch.zeros(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
                      dtype=torch.uint8, device="cuda")
 
     def steps():
