@@ -169,6 +169,25 @@ int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_ca
                                       int head_dim, int block_size, int num_blocks, int window, float scale,
                                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * pkv_paged_attention_decode, with the same arguments minus the workspace.
+ * The partial results live in a device array of this library, one copy per
+ * GPU, PKV_DECODE_SCRATCH_BYTES large and held until the process ends; its
+ * address is looked up on the first call on each device.  The call makes no
+ * allocation of any kind.  A batch whose partials need more than that
+ * (pkv_decode_workspace_size above it) returns PKV_ERR_WORKSPACE and
+ * launches nothing.  Every call on one GPU shares its array: calls that may
+ * run at the same time on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.  Nothing in the array needs to start at
+ * zero; it keeps the last call's contents. */
+#define PKV_DECODE_SCRATCH_BYTES (32u << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------
  * paged_attention_prefill: a causal query chunk over a cached prefix.
  * Query i of sequence s (rows cu_q_lens[s] .. cu_q_lens[s+1]-1 of q) sits at

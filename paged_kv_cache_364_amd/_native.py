@@ -60,6 +60,8 @@ SIGNATURES = {
                                            c_int, c_float, c_int, vp, c_size, vp]),
     "pkv_paged_attention_decode_window": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                                   c_int, c_int, c_float, c_int, vp, c_size, vp]),
+    "pkv_paged_attention_decode_noalloc": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int,
+                                                   c_int, c_int, c_float, c_int, vp]),
     "pkv_paged_attention_prefill": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp, c_int, vp, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_float, c_int, vp]),
     "pkv_gather_units": (c_int, [vp, vp, vp, c_int, c_int, c_i64, vp, c_int, vp]),

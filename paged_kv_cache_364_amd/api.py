@@ -143,6 +143,26 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     return out
 
 
+def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   scale: float, stream=None) -> torch.Tensor:
+    """As paged_attention_decode, with the partials in the library's own
+    per-GPU scratch array (pkv_paged_attention_decode_noalloc): no
+    allocation anywhere, for callers that cannot allocate."""
+    N_, H, B, D = _cache_geometry(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q/out must be [num_seqs, num_heads, head_dim] of the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    N.check(N.lib().pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, H, D, B, N_, float(scale), _dtype_code(q),
+        _stream(stream)), "paged_attention_decode_noalloc")
+    return out
+
+
 def gather_units(pool_a: torch.Tensor, pool_b: Optional[torch.Tensor], unit_ids: torch.Tensor, unit_kib: int,
                  sink: torch.Tensor, stream=None) -> None:
     """Read every listed unit of unit_kib KiB of pool_a (and pool_b) once,

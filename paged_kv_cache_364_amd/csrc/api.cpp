@@ -9,6 +9,8 @@
 #include "../../include/pagedkv.h"
 #include "kernels.h"
 
+static_assert(PKV_DECODE_SCRATCH_BYTES == pkv::kDecodeScratchBytes, "header and library disagree on the scratch size");
+
 namespace pkv {
 
 const DeviceInfo& device_info() {
@@ -196,6 +198,26 @@ int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_ca
   return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, window, scale, dtype, workspace,
                      workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                                       void* stream) {
+  if (num_kv_heads <= 0) return PKV_ERR_INVALID;
+  int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           dtype);
+  if (st) return st;
+  if (!pkv::decode_supported(dtype, head_dim, num_heads / num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
+      !aligned4(context_lens))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_decode_scratch(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                    num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                                    (hipStream_t)stream);
 }
 
 int pkv_gather_units(const void* pool_a, const void* pool_b, const int32_t* unit_ids, int num_units, int unit_kib,

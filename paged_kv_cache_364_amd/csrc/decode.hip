@@ -34,6 +34,8 @@
 // and head; softmax weights reach the P.V lanes through 256 bytes of LDS.
 // P.V accumulates in fp32 registers; row groups are combined once per
 // segment.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -772,6 +774,44 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   hipLaunchKernelGGL((void (*)(DecodeArgs))k.merge, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -6;
   return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the partials and merge jobs live in a
+// fixed device array of this library (one copy per GPU, held until the
+// process ends).  In host code the array's name is only a stand-in for the
+// symbol; its device address, which differs per GPU, is looked up once per
+// device and that address is what the kernels receive.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+static void* scratch_address(int dev) {
+  static void* addr[64] = {};
+  static std::mutex mu;
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+int launch_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
+                          int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
+                          float scale, int dtype, hipStream_t stream) {
+  DecodeKernels k;
+  if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
+  size_t jobs_off;
+  if (workspace_layout(k, decode_waves(k, S, Hkv, max_blocks, B), &jobs_off) > (size_t)kDecodeScratchBytes)
+    return -7;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -6;
+  void* ws = scratch_address(dev);
+  if (ws == nullptr) return -6;
+  return launch_decode(out, q, k_cache, v_cache, tables, max_blocks, ctx, S, Hq, Hkv, D, B, num_blocks, 0, scale,
+                       dtype, ws, (size_t)kDecodeScratchBytes, stream);
 }
 
 }  // namespace pkv

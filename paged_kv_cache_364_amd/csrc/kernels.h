@@ -41,6 +41,12 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
                   int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Size of the library's own decode scratch array (per GPU).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+int launch_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
+                          int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
+                          float scale, int dtype, hipStream_t stream);
+
 bool prefill_supported(int dtype, int head_dim, int group, int block_size);
 int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
                    const void* k_cache, const void* v_cache, const int32_t* tables, int max_blocks,
