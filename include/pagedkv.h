@@ -213,6 +213,42 @@ int pkv_paged_attention_prefill(void* out, const void* q, const int32_t* cu_q_le
                                 float scale, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * paged_attention_decode_shared: decode for a batch whose sequences share a
+ * prompt (parallel sampling, beam search).  Branches forked from one prompt
+ * hold its blocks together, by reference count (intelliparadigm.com
+ * article, section 2.3; "08. PagedAttention", section "what else paging
+ * solves"); the pages store such a prompt once (cnblogs "paged attention",
+ * section 9), and this call also reads it once per step: the query heads of
+ * all members of a group are stacked against each shared block.  The result
+ * is that of pkv_paged_attention_decode on the same inputs (the same
+ * formula; only the order of the sums differs).
+ *
+ *   group_start    device int32 [num_groups + 1]: group i is the sequences
+ *                  group_start[i] .. group_start[i+1] - 1 of the batch;
+ *                  group_start[0] = 0, increasing, group_start[num_groups] =
+ *                  num_seqs; each group holds 1 ..
+ *                  pkv_decode_shared_max_members(num_heads, num_kv_heads)
+ *                  sequences (members past that come out NaN)
+ *   shared_blocks  device int32 [num_groups]: the number of leading table
+ *                  entries that are the same block in every member of the
+ *                  group and lie wholly inside every member's context
+ *                  (pkv_shared_prefix_groups computes both arrays)
+ * Other arguments as pkv_paged_attention_decode; no workspace: one launch,
+ * one workgroup per (group, kv head).  bf16, head_dim 128, block_size a
+ * power of two from 16 to 256 (PKV_ERR_UNSUPPORTED otherwise).
+ * ---------------------------------------------------------------------- */
+int pkv_paged_attention_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens, int num_seqs, const int32_t* group_start,
+                                      const int32_t* shared_blocks, int num_groups, int num_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                                      void* stream);
+
+/* Largest group pkv_paged_attention_decode_shared takes for this head
+ * layout: min(8, 16 / (num_heads / num_kv_heads)); 0 for an invalid one. */
+int pkv_decode_shared_max_members(int num_heads, int num_kv_heads);
+
+/* ------------------------------------------------------------------------
  * gather_units: a measurement aid, not part of the attention path.  Reads
  * every listed unit once and computes nothing else, so its rate is the HBM
  * bandwidth ceiling of the paged access pattern (a table lookup, then a
@@ -347,6 +383,19 @@ int pkv_get_block_table(const pkv_alloc* a, int64_t seq, int32_t* out, int cap, 
  * (pad -1), context_lens_out host int32 [num_seqs]. */
 int pkv_build_block_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs,
                            int max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
+
+/* Groups of a batch for pkv_paged_attention_decode_shared (forks of one
+ * prompt hold its blocks together: intelliparadigm.com article, section
+ * 2.3).  Walking the batch in order, a group is a sequence and the ones
+ * right after it whose first table entry is the same physical block, at
+ * most max_members of them; its shared block count is the number of leading
+ * table entries that are the same live block in every member and lie
+ * wholly inside every member's context (0 for a one-member group).
+ *   group_start_out    host int32 [num_seqs + 1] (num_groups + 1 written)
+ *   shared_blocks_out  host int32 [num_seqs] (num_groups written)
+ * PKV_ERR_INVALID for an unknown sequence, PKV_ERR_STATE for a swapped one. */
+int pkv_shared_prefix_groups(const pkv_alloc* a, const int64_t* seqs, int num_seqs, int max_members,
+                             int32_t* group_start_out, int32_t* shared_blocks_out, int* num_groups_out);
 
 int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out);
 

@@ -383,6 +383,37 @@ class BlockAllocator:
     def used_blocks(self) -> set:
         return {b for b in range(self.num_blocks) if self.ref[b] > 0}
 
+    def shared_prefix_groups(self, seqs: Sequence[int], max_members: int):
+        """Groups of a batch for the shared-prefix decode.  A group is a
+        sequence and the ones right after it in the batch whose first table
+        entry is the same physical block (forks of one prompt hold it
+        together: intelliparadigm.com article, section 2.3), at most
+        max_members; its shared length is the number of leading table
+        entries that are the same live block in every member and lie wholly
+        inside every member's context.  A one-member group shares nothing.
+        Returns (group_start [num_groups + 1], shared_blocks [num_groups])."""
+        B = self.block_size
+        starts, shared = [], []
+        i, n = 0, len(seqs)
+        while i < n:
+            first = self.tables[seqs[i]]
+            j = i + 1
+            while (j < n and j - i < max_members and first and first[0] >= 0
+                   and self.tables[seqs[j]] and self.tables[seqs[j]][0] == first[0]):
+                j += 1
+            k = 0
+            if j - i > 1:
+                members = seqs[i:j]
+                while (k < len(first) and first[k] >= 0
+                       and all(k < len(self.tables[m]) and self.tables[m][k] == first[k]
+                               and (k + 1) * B <= self.lens[m] for m in members)):
+                    k += 1
+            starts.append(i)
+            shared.append(k)
+            i = j
+        starts.append(n)
+        return starts, shared
+
     def block_tables(self, seqs: Sequence[int], width: int):
         """Padded [len(seqs), width] table (pad -1) and context lengths."""
         import numpy as np

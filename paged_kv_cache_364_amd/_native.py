@@ -65,6 +65,10 @@ SIGNATURES = {
     "pkv_paged_attention_prefill": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp, c_int, vp, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_float, c_int, vp]),
     "pkv_gather_units": (c_int, [vp, vp, vp, c_int, c_int, c_i64, vp, c_int, vp]),
+    "pkv_paged_attention_decode_shared": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, vp, vp, c_int, c_int, c_int,
+                                                  c_int, c_int, c_int, c_float, c_int, vp]),
+    "pkv_decode_shared_max_members": (c_int, [c_int, c_int]),
+    "pkv_shared_prefix_groups": (c_int, [vp, i64p, c_int, c_int, i32p, i32p, intp]),
     "pkv_alloc_create": (vp, [c_int, c_int, i32p]),
     "pkv_alloc_destroy": (None, [vp]),
     "pkv_seq_add": (c_int, [vp, c_i64]),

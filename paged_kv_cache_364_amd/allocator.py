@@ -132,6 +132,19 @@ class BlockAllocator:
                 "build_block_tables")
         return t, lens
 
+    def shared_prefix_groups(self, seqs: Sequence[int], max_members: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Groups of the batch for the shared-prefix decode
+        (pkv_shared_prefix_groups): group_start [num_groups + 1] and
+        shared_blocks [num_groups], both int32."""
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        starts = np.empty(len(ids) + 1, dtype=np.int32)
+        shared = np.empty(max(len(ids), 1), dtype=np.int32)
+        ng = ctypes.c_int(0)
+        N.check(self._L.pkv_shared_prefix_groups(self._h, ids.ctypes.data_as(N.i64p), len(ids), int(max_members),
+                                                 starts.ctypes.data_as(N.i32p), shared.ctypes.data_as(N.i32p),
+                                                 ctypes.byref(ng)), "shared_prefix_groups")
+        return starts[: ng.value + 1].copy(), shared[: ng.value].copy()
+
     def stats(self) -> N.PkvStats:
         s = N.PkvStats()
         N.check(self._L.pkv_alloc_stats(self._h, ctypes.byref(s)), "alloc_stats")

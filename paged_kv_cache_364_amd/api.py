@@ -163,6 +163,37 @@ def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: 
     return out
 
 
+def decode_shared_max_members(num_heads: int, num_kv_heads: int) -> int:
+    """Largest group paged_attention_decode_shared takes (pkv_decode_shared_max_members)."""
+    return int(N.lib().pkv_decode_shared_max_members(int(num_heads), int(num_kv_heads)))
+
+
+def paged_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor, group_start: torch.Tensor,
+                                  shared_blocks: torch.Tensor, scale: float, stream=None) -> torch.Tensor:
+    """Decode of a batch whose sequences share prompt blocks, each group's
+    shared blocks read once for all its members
+    (pkv_paged_attention_decode_shared); group_start int32 [num_groups + 1]
+    and shared_blocks int32 [num_groups] as BlockAllocator.shared_prefix_groups
+    returns them, on the GPU."""
+    N_, H, B, D = _cache_geometry(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q/out must be [num_seqs, num_heads, head_dim] of the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    G = shared_blocks.numel()
+    if group_start.shape != (G + 1,):
+        raise ValueError("group_start must be [num_groups + 1]")
+    N.check(N.lib().pkv_paged_attention_decode_shared(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, _dev(group_start, "group_start", torch.int32),
+        _dev(shared_blocks, "shared_blocks", torch.int32), G, Hq, H, D, B, N_, float(scale), _dtype_code(q),
+        _stream(stream)), "paged_attention_decode_shared")
+    return out
+
+
 def gather_units(pool_a: torch.Tensor, pool_b: Optional[torch.Tensor], unit_ids: torch.Tensor, unit_kib: int,
                  sink: torch.Tensor, stream=None) -> None:
     """Read every listed unit of unit_kib KiB of pool_a (and pool_b) once,

@@ -532,6 +532,54 @@ int pkv_build_block_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs
   return PKV_OK;
 }
 
+int pkv_shared_prefix_groups(const pkv_alloc* a, const int64_t* seqs, int num_seqs, int max_members,
+                             int32_t* group_start_out, int32_t* shared_blocks_out, int* num_groups_out) {
+  if (!a || num_seqs < 0 || max_members < 1 || !num_groups_out) return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!seqs || !group_start_out || !shared_blocks_out)) return PKV_ERR_INVALID;
+  std::vector<const pkv_alloc::Seq*> ss((size_t)num_seqs);
+  for (int i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seqs[i]);
+    if (it == a->seqs.end()) return PKV_ERR_INVALID;
+    if (it->second.swapped) return PKV_ERR_STATE;
+    ss[(size_t)i] = &it->second;
+  }
+  const int64_t B = a->block_size;
+  int ng = 0;
+  int i = 0;
+  while (i < num_seqs) {
+    // a group: this sequence and the ones right after it that hold the same
+    // physical block as their first block (forks of one prompt), up to
+    // max_members
+    const std::vector<int32_t>& t0 = ss[(size_t)i]->table;
+    int j = i + 1;
+    while (j < num_seqs && j - i < max_members && !t0.empty() && t0[0] >= 0 && !ss[(size_t)j]->table.empty() &&
+           ss[(size_t)j]->table[0] == t0[0])
+      ++j;
+    // shared: the longest common prefix of the members' tables, of live
+    // blocks wholly inside every member's context
+    int64_t k = 0;
+    if (j - i > 1) {
+      for (;; ++k) {
+        if (k >= (int64_t)t0.size() || t0[(size_t)k] < 0) break;
+        bool same = true;
+        for (int m = i; m < j && same; ++m) {
+          const pkv_alloc::Seq& s = *ss[(size_t)m];
+          same = k < (int64_t)s.table.size() && s.table[(size_t)k] == t0[(size_t)k] && (k + 1) * B <= s.len;
+        }
+        if (!same) break;
+      }
+    }
+    group_start_out[ng] = i;
+    shared_blocks_out[ng] = (int32_t)k;
+    ++ng;
+    i = j;
+  }
+  if (num_seqs > 0) group_start_out[ng] = num_seqs;
+  else group_start_out[0] = 0;
+  *num_groups_out = ng;
+  return PKV_OK;
+}
+
 int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out) {
   if (!a || !out) return PKV_ERR_INVALID;
   out->num_blocks = a->num_blocks;

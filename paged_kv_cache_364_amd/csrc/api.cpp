@@ -220,6 +220,36 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_c
                                     (hipStream_t)stream);
 }
 
+int pkv_decode_shared_max_members(int num_heads, int num_kv_heads) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return 0;
+  return pkv::max_shared_members(num_heads / num_kv_heads);
+}
+
+int pkv_paged_attention_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens, int num_seqs, const int32_t* group_start,
+                                      const int32_t* shared_blocks, int num_groups, int num_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks, float scale, int dtype,
+                                      void* stream) {
+  if (num_kv_heads <= 0) return PKV_ERR_INVALID;
+  int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           dtype);
+  if (st) return st;
+  if (num_groups < 0 || num_groups > num_seqs) return PKV_ERR_INVALID;
+  if (!pkv::decode_shared_supported(dtype, head_dim, num_heads / num_kv_heads, block_size))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_groups == 0) return PKV_ERR_INVALID;  // groups must cover the batch
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_start || !shared_blocks)
+    return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || !aligned4(group_start) || !aligned4(shared_blocks))
+    return PKV_ERR_ALIGN;
+  return pkv::launch_decode_shared(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                   group_start, shared_blocks, num_groups, num_heads, num_kv_heads, head_dim,
+                                   block_size, num_blocks, scale, (hipStream_t)stream);
+}
+
 int pkv_gather_units(const void* pool_a, const void* pool_b, const int32_t* unit_ids, int num_units, int unit_kib,
                      int64_t pool_units, void* sink, int sink_words, void* stream) {
   if (num_units < 0 || pool_units <= 0 || sink_words < 4) return PKV_ERR_INVALID;

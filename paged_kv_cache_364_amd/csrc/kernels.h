@@ -47,6 +47,13 @@ int launch_decode_scratch(void* out, const void* q, const void* k_cache, const v
                           int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
                           float scale, int dtype, hipStream_t stream);
 
+bool decode_shared_supported(int dtype, int head_dim, int group, int block_size);
+int max_shared_members(int group);
+int launch_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
+                         int max_blocks, const int32_t* ctx, int S, const int32_t* group_start,
+                         const int32_t* shared_blocks, int num_groups, int Hq, int Hkv, int D, int B, int num_blocks,
+                         float scale, hipStream_t stream);
+
 bool prefill_supported(int dtype, int head_dim, int group, int block_size);
 int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
                    const void* k_cache, const void* v_cache, const int32_t* tables, int max_blocks,

@@ -266,15 +266,17 @@ PROMPT_SEQ_BASE = 10_000
 
 
 def shared_prefix(seed=4, num_prompts=32, prompt_len=1024, n_branches=4, fork_lo=1000,
-                  fork_hi=1023, priv_hi=256, num_blocks=25_600, name=None, fork_points=None):
+                  fork_hi=1023, priv_hi=256, num_blocks=25_600, name=None, fork_points=None, block_size=16,
+                  heads=None):
     """Parallel sampling: each prompt is forked into ``n_branches`` branches at
     a point f drawn uniformly from fork_lo..fork_hi minus the multiples of the
     block size; the prompt is then released, so the
     branches hold the shared blocks alone.  Each branch writes p ~ U{0..priv_hi}
     private tokens, then one decode token (context f + p + 1)."""
     rng = np.random.default_rng(seed)
-    bsz = 16
-    hkv, d = LLAMA["num_kv_heads"], LLAMA["head_dim"]
+    bsz = block_size
+    hd = dict(LLAMA) if heads is None else dict(heads)
+    hkv, d = hd["num_kv_heads"], hd["head_dim"]
     if fork_points is None:
         # uniform over the fork points inside a block, so that every branch's
         # first write lands in a shared, partly filled block and forces a
@@ -289,7 +291,7 @@ def shared_prefix(seed=4, num_prompts=32, prompt_len=1024, n_branches=4, fork_lo
     nseq = num_prompts * n_branches
     priv = rng.integers(0, priv_hi + 1, size=nseq)
     init_order = rng.permutation(num_blocks).astype(np.int32)
-    q = _values(rng, (nseq, LLAMA["num_heads"], d), BF16)
+    q = _values(rng, (nseq, hd["num_heads"], d), BF16)
     kp = _values(rng, (num_prompts, prompt_len, hkv, d), BF16)
     vp = _values(rng, (num_prompts, prompt_len, hkv, d), BF16)
     tot = int(priv.sum())
@@ -317,7 +319,7 @@ def shared_prefix(seed=4, num_prompts=32, prompt_len=1024, n_branches=4, fork_lo
     dstep = Step([Op("append", s, n=1, k=kn[s: s + 1], v=vn[s: s + 1]) for s in range(nseq)])
     mb = -(-(fork_hi + priv_hi + 1) // bsz)
     return Workload(name or f"llama31-8b-shared-prefix-{num_prompts}x{n_branches}", "decode", BF16,
-                    **LLAMA, block_size=bsz, num_blocks=num_blocks, scale=_scale(d),
+                    **hd, block_size=bsz, num_blocks=num_blocks, scale=_scale(d),
                     init_order=init_order, steps=[a, b, c, dstep], batch=list(range(nseq)), q=q,
                     max_blocks_per_seq=mb)
 

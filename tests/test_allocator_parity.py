@@ -29,7 +29,7 @@ def same_state(a: BlockAllocator, o: OracleAlloc):
     assert a.prefix_cache_size() == len(o.cache)
 
 
-def run_both(wl):
+def run_both(wl, groups=(8, 4, 2, 1)):
     a = BlockAllocator(wl.num_blocks, wl.block_size, wl.init_order)
     o = OracleAlloc(wl.num_blocks, wl.block_size, wl.init_order)
     for st in wl.steps:
@@ -56,6 +56,11 @@ def run_both(wl):
     t2, l2 = o.block_tables(wl.batch, wl.max_blocks_per_seq)
     assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
     same_state(a, o)
+    for mm in groups:
+        gs1, sb1 = a.shared_prefix_groups(wl.batch, mm)
+        gs2, sb2 = o.shared_prefix_groups(wl.batch, mm)
+        assert gs1.tolist() == gs2 and sb1.tolist() == sb2, mm
+    return a, o
 
 
 def test_tiny_f32_decode_script():
@@ -330,3 +335,17 @@ def test_errors_leave_state_unchanged():
         BlockAllocator(0, 4)
     with pytest.raises(PagedKVError):
         a.block_tables([0], 2)  # table of 3 blocks does not fit 2 columns
+
+
+def test_shared_prefix_groups_match_on_forks():
+    """Groups for the shared-prefix decode, C++ against the oracle, on
+    parallel-sampling batches with forks in and on block edges, of several
+    block sizes, and on the full 32 x 4 batch."""
+    for bs, forks in ((16, [40, 48, 33]), (32, [64, 70, 95]), (64, [64, 100, 127])):
+        wl = W.shared_prefix(31 + bs, num_prompts=3, prompt_len=128, n_branches=3, fork_points=forks,
+                             priv_hi=40, num_blocks=512, block_size=bs)
+        run_both(wl)
+    a, o = run_both(W.llama_shared_prefix_32x4(), groups=(4,))
+    gs, sb = a.shared_prefix_groups(W.llama_shared_prefix_32x4().batch, 4)
+    assert gs.tolist() == list(range(0, 129, 4))
+    assert all(61 <= x <= 63 for x in sb.tolist())

@@ -247,3 +247,27 @@ def test_bf16_shift_mistake_is_caught(monkeypatch):
 def test_bf16_read_as_fp16_is_caught(monkeypatch):
     monkeypatch.setattr(attention, "to_f64", _to_f64_with(as_fp16=True))
     assert fails(P.check_bf16_decoding)
+
+
+def test_shared_prefix_past_a_member_context_is_caught(monkeypatch):
+    """A grouping that shares a block some member's context ends inside."""
+    def groups(self, seqs, max_members):
+        starts, shared = [], []
+        i, n = 0, len(seqs)
+        while i < n:
+            first = self.tables[seqs[i]]
+            j = i + 1
+            while j < n and j - i < max_members and first and self.tables[seqs[j]][:1] == first[:1]:
+                j += 1
+            k = 0
+            if j - i > 1:
+                while k < len(first) and all(k < len(self.tables[m]) and self.tables[m][k] == first[k]
+                                             for m in seqs[i:j]):
+                    k += 1
+            starts.append(i)
+            shared.append(k)
+            i = j
+        starts.append(n)
+        return starts, shared
+    monkeypatch.setattr(BlockAllocator, "shared_prefix_groups", groups)
+    assert fails(P.check_shared_prefix_groups)

@@ -577,6 +577,46 @@ def test_shared_prefix_full_config_forces_copies():
     assert len(copies) == 3 * 32
 
 
+def check_shared_prefix_groups():
+    """Worked cases, by hand, for the grouping of the shared-prefix decode
+    (B = 16).  A 40-token prompt fills blocks p0, p1 and 8 slots of p2."""
+    a = BlockAllocator(64, 16, list(range(64)))
+    a.add(100)
+    a.append(100, 40)
+    p0, p1, p2 = a.table(100)
+    # three branches at the end of the prompt, one at position 20 (inside p1)
+    for c, f in ((0, 40), (1, 40), (2, 40), (3, 20)):
+        a.fork(100, c, f)
+    a.add(4)
+    a.append(4, 5)                # an unrelated request
+    a.release(100)
+    for c in (0, 1, 2):
+        a.append(c, 1)            # each writes at 40: two copy p2, the last writes in place
+    a.append(3, 1)                # writes at 20, inside shared p1: copied
+    assert [a.table(c)[:2] for c in (0, 1, 2)] == [[p0, p1]] * 3
+    assert len({a.table(c)[2] for c in (0, 1, 2)}) == 3
+    starts, shared = a.shared_prefix_groups([0, 1, 2, 3, 4], 8)
+    # branch 3 copied p1 (its write at 20), so it shares only p0 with them
+    assert starts == [0, 4, 5] and shared == [1, 0]
+    # without branch 3's write, p1 would still be one block shared by all
+    # four, but branch 3's context (21 tokens) ends inside it: not shared
+    b = BlockAllocator(64, 16, list(range(64)))
+    b.add(100)
+    b.append(100, 40)
+    for c, f in ((0, 40), (1, 40), (3, 20)):
+        b.fork(100, c, f)
+    assert b.shared_prefix_groups([0, 1, 3], 8) == ([0, 3], [1])
+    assert b.shared_prefix_groups([0, 1], 8) == ([0, 2], [2])
+    # the member bound splits a run; a lone member shares nothing
+    assert a.shared_prefix_groups([0, 1, 2], 2) == ([0, 2, 3], [2, 0])
+    assert a.shared_prefix_groups([4, 0, 1], 8) == ([0, 1, 3], [0, 2])
+    assert a.shared_prefix_groups([], 4) == ([0], [])
+
+
+def test_shared_prefix_groups_worked_cases():
+    check_shared_prefix_groups()
+
+
 def test_ragged_lengths_and_churn():
     wl = W.ragged_decode(3, num_seqs=64, num_blocks=4096, churn_ops=300)
     st = runner.run(wl, with_pools=False)
