@@ -350,6 +350,24 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
                                        float(wl.scale), workspace=ws)
 
         ms, all_ms = timed_calls(torch, decode, steps, warmup, stream)
+        shared = None
+        if build is workloads.llama_shared_prefix_32x4:
+            # the same batch through the shared-prefix decode: each prompt's
+            # shared blocks read once for its branches
+            gs, sb = st.alloc.shared_prefix_groups(wl.batch, api.decode_shared_max_members(Hq, Hkv))
+            gsd, sbd = torch.from_numpy(gs).to(dev), torch.from_numpy(sb).to(dev)
+
+            def decode_shared(i):
+                api.paged_attention_decode_shared(out, q, kps[i % layers], vps[i % layers], st.tables_dev,
+                                                  st.lens_dev, gsd, sbd, float(wl.scale))
+
+            sms, _ = timed_calls(torch, decode_shared, steps, warmup, stream, per_call=False)
+            shared = {"call": "paged_attention_decode_shared", "groups": int(len(sb)),
+                      "shared_blocks_per_group": [int(sb.min()), int(sb.max())],
+                      "decode_us_avg": round(sms * 1e3, 2),
+                      "kv_gbps_unique": round(uniq_bytes / (sms * 1e-3) / 1e9, 1),
+                      "pct_hbm_peak_unique": round(100 * uniq_bytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                      "seqs_per_s_per_layer": round(S / (sms * 1e-3), 1)}
         r = {"workload": wl.name, "batch": desc, "num_seqs": S, "sum_context": int(lens.sum()),
              "layers_rotated": layers, "decode_us_avg": round(ms * 1e3, 2),
              "decode_us_per_call_events_median": round(float(np.median(all_ms)) * 1e3, 2),
@@ -357,6 +375,9 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
              "kv_bytes_unique": uniq_bytes, "kv_gbps_unique": round(uniq_bytes / (ms * 1e-3) / 1e9, 1),
              "pct_hbm_peak_unique": round(100 * uniq_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
              "seqs_per_s_per_layer": round(S / (ms * 1e-3), 1)}
+        if shared is not None:
+            r["plain_call"] = "paged_attention_decode (every branch streams its prefix)"
+            r["shared_prefix_decode"] = shared
         log(f"{wl.name}: {r}")
         res[wl.name] = r
         del st, kps, vps, q, out, ws

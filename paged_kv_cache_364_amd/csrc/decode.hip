@@ -495,12 +495,23 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     }
   }
 
-  // chunks per kv head, and this wavefront's share [gstart, gend)
-  int W1 = 0;
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    W1 += wave_sum_i(s < S ? chunks_of(a.ctx_lens[s], maxctx, NT, a.window) : 0);
+  // Chunks per kv head, and this wavefront's share [gstart, gend), in two
+  // round trips whatever the batch size: lane l first sums the chunks of
+  // its own contiguous segment of sequences (all of its loads in flight at
+  // once), a scan over the 64 segments finds the one holding chunk gstart,
+  // and one more load of that segment finds the sequence.
+  const int seg = (S + 63) / 64;  // sequences per lane segment
+  const int sbeg = min(lane * seg, S), send = min(sbeg + seg, S);
+  int my_n = 0;
+  for (int si = sbeg; si < send; si += 8) {
+    int cx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cx[j] = si + j < send ? a.ctx_lens[si + j] : 0;  // all eight loads in flight
+#pragma unroll
+    for (int j = 0; j < 8; ++j) my_n += chunks_of(cx[j], maxctx, NT, a.window);
   }
+  const int seg_incl = wave_incl_scan_i(my_n, lane);
+  const int W1 = __builtin_amdgcn_readlane(seg_incl, 63);
   const int Wtot = a.Hkv * W1;
   const int cpw = (Wtot + a.nW - 1) / max(a.nW, 1);
   const int gstart = w * cpw;
@@ -510,22 +521,31 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   int h = gstart / W1;
   const int rem = gstart - h * W1;
   int s = 0, P = 0;
-  bool found = false;
-  for (int base = 0; base < S; base += 64) {
-    const int si = base + lane;
-    const int n = si < S ? chunks_of(a.ctx_lens[si], maxctx, NT, a.window) : 0;
-    const int incl = wave_incl_scan_i(n, lane);
-    const unsigned long long hit = __ballot(P + incl > rem);
-    if (hit) {
-      const int first = __ffsll((long long)hit) - 1;
-      s = base + first;
-      P += __shfl(incl - n, first);
-      found = true;
-      break;
+  {
+    const unsigned long long seg_hit = __ballot(seg_incl > rem);
+    if (!seg_hit) return;  // context lengths changed under the kernel: do nothing
+    const int ls = __ffsll((long long)seg_hit) - 1;  // lane whose segment holds it
+    const int base = ls * seg;
+    P = __builtin_amdgcn_readlane(seg_incl - my_n, ls);
+    // the segment (at most 64 sequences for batches up to 4,096; longer
+    // segments are walked 64 at a time)
+    bool found = false;
+    for (int b0 = base; b0 < min(base + seg, S) && !found; b0 += 64) {
+      const int si = b0 + lane;
+      const int n = si < min(base + seg, S) ? chunks_of(a.ctx_lens[si], maxctx, NT, a.window) : 0;
+      const int incl = wave_incl_scan_i(n, lane);
+      const unsigned long long hit = __ballot(P + incl > rem);
+      if (hit) {
+        const int first = __ffsll((long long)hit) - 1;
+        s = b0 + first;
+        P += __builtin_amdgcn_readlane(incl - n, first);
+        found = true;
+      } else {
+        P += __builtin_amdgcn_readlane(incl, 63);
+      }
     }
-    P += __shfl(incl, 63);
+    if (!found) return;
   }
-  if (!found) return;  // context lengths changed under the kernel: do nothing
 
   Unit<T, D, G> cur, nxt;
   int c = rem - P;  // chunk of `cur` being computed

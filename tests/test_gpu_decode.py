@@ -249,3 +249,32 @@ def test_workspace_reused_across_calls_and_garbage_filled():
             first = got
         elif i % 2 == 0:
             assert np.array_equal(got, first), "repeated call differs"
+
+
+@pytest.mark.parametrize("n,hi", [(2048, 64), (4100, 24)])
+def test_many_short_sequences(n, hi):
+    """Batches of thousands of short contexts (1 .. hi tokens): the start of
+    the decode finds each wavefront's first chunk in two round trips (lane
+    segments, then one segment), whatever the batch size; 4,100 sequences
+    make segments longer than one wavefront load.  Outputs against the
+    oracle; the call's time is printed."""
+    rng = np.random.default_rng(900 + n)
+    lens = [int(x) for x in rng.integers(1, hi + 1, size=n)]
+    wl = W.decode_workload(f"short-{n}", 901 + n, lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                           num_blocks=8192, dtype="bf16")
+    st, ost, out = check_workload(wl, pools_too=False)
+    q = driver.to_device(wl.q, "bf16", "cuda")
+    ws = torch.empty(api.decode_workspace_size(n, 32, 8, 128, 16, wl.max_blocks_per_seq, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        api.paged_attention_decode(out, q, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev, float(wl.scale),
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        api.paged_attention_decode(out, q, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev, float(wl.scale),
+                                   workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    say(f"[gpu] {n} sequences of 1..{hi} tokens ({sum(lens)} in all): {e0.elapsed_time(e1) / 20 * 1e3:.1f} us per call")
