@@ -37,6 +37,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
 # paged_kv_cache_364_amd.profiling from two --pmc runs of this script)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama31_8b_b64_prefill_opt13b_b16x512.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util_prefill_opt13b_b16x512.txt")
+SHARED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_llama_shared_prefix_32x4.txt")
 
 
 def log(msg):
@@ -325,7 +326,7 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
     stream = torch.cuda.current_stream()
     for build, desc in ((workloads.llama_ragged_b256, "256 contexts, log-normal (median 500, sigma 1, clip 1..8192), "
                                             "churned free list (seed 3)"),
-                        (workloads.llama_shared_prefix_32x4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023}, "
+                        (workloads.llama_shared_prefix_32x4, "32 prompts x 1,024 tokens forked into 4 branches at U{1000..1023} minus 1008 (never on a block edge), "
                                             "U{0..256} private tokens each (seed 4)")):
         if only is not None and build.__name__ != only:
             continue
@@ -368,6 +369,10 @@ def other_batch_legs(torch, np, api, driver, workloads, dev, steps, warmup, laye
                       "kv_gbps_unique": round(uniq_bytes / (sms * 1e-3) / 1e9, 1),
                       "pct_hbm_peak_unique": round(100 * uniq_bytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                       "seqs_per_s_per_layer": round(S / (sms * 1e-3), 1)}
+            from paged_kv_cache_364_amd import profiling
+            tb = profiling.traffic_bytes(profiling.read_traffic(SHARED_TRAFFIC_FILE), ["decode_shared_kernel<128>"])
+            shared["traffic"] = int(round(tb)) if tb is not None else None
+            shared["traffic_over_unique"] = round(tb / uniq_bytes, 4) if tb is not None else None
         r = {"workload": wl.name, "batch": desc, "num_seqs": S, "sum_context": int(lens.sum()),
              "layers_rotated": layers, "decode_us_avg": round(ms * 1e3, 2),
              "decode_us_per_call_events_median": round(float(np.median(all_ms)) * 1e3, 2),

@@ -35,6 +35,7 @@ from typing import Dict, List
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "decode": ["csrc/decode.hip", "csrc/common.h"],
+    "decode_shared": ["csrc/decode_shared.hip", "csrc/common.h"],
     "prefill": ["csrc/prefill.hip", "csrc/common.h"],
     "cache_ops": ["csrc/cache_ops.hip", "csrc/common.h"],
 }
@@ -50,11 +51,13 @@ def sources_sha(group: str) -> str:
 
 
 def kernel_group(name: str) -> str:
+    if "decode_shared" in name:
+        return "decode_shared"
     if "decode_" in name:
         return "decode"
     if "prefill_" in name:
         return "prefill"
-    if "kv_write" in name or "copy_blocks" in name:
+    if "kv_write" in name or "copy_blocks" in name or "gather_units" in name:
         return "cache_ops"
     return ""
 
