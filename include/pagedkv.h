@@ -257,8 +257,9 @@ int pkv_decode_shared_max_members(int num_heads, int num_kv_heads);
  *
  *   pool_a, pool_b   device pools of pool_units units of unit_kib KiB each
  *                    (pool_b may be NULL; when given, unit i is read from both)
- *   unit_ids         device int32 [num_units]: units to read; ids outside
- *                    [0, pool_units) are skipped
+ *   unit_ids         device int32 [num_units]: units to read; an id outside
+ *                    [0, pool_units) reads unit 0 instead (nothing outside
+ *                    the pools is ever read)
  *   unit_kib         a power of two from 1 to 4096
  *   sink             device uint32 [sink_words], sink_words >= 4: one folded
  *                    word per wavefront (keeps the loads live; no meaning)

@@ -148,69 +148,64 @@ int launch_swap_blocks(bool out, void* k_cache, void* v_cache, const int32_t* id
 // loads and folded into one word per wavefront, with no other arithmetic.
 // This is the access pattern of the decode (block-table lookups, then
 // contiguous runs of K and V) without its computation, so its rate is the
-// bandwidth ceiling that pattern can reach on the device.  Persistent grid
-// of six 4-wavefront workgroups per compute unit (the fastest shape of a
-// sweep over 2..12): wavefront w takes an equal contiguous share of the
-// 1 KiB pieces of all units; a window of 64 unit ids is held in a register,
-// and the loads of the next four pieces (of each pool) are in flight while
-// the current four are folded.
+// bandwidth ceiling that pattern can reach on the device.
+//
+// The units are cut into items of P KiB (P = min(4, unit KiB)); wavefront w
+// takes an equal contiguous share of the items.  Unit ids come through the
+// scalar cache, so waiting for an id never waits for the data loads (vector
+// loads complete in order), and the loads of an item are issued
+// unconditionally (an id outside the pool reads unit 0), so the compiler
+// keeps them in the registers they are folded from instead of copying them
+// there, which would wait for every load in flight.  One item per wavefront
+// is in flight while the previous one is folded; eight wavefronts per
+// compute unit (two workgroups) was the fastest shape of a sweep over 4..32
+// wavefronts and 1..4 items in flight.
 __device__ __forceinline__ uint4 gather_load(const void* p) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+typedef __attribute__((address_space(4))) const int32_t sconst_i32_gather;
+
+template <int P, bool TWO>
 __global__ __launch_bounds__(256) void gather_units_kernel(const char* __restrict__ pa, const char* __restrict__ pb,
-                                                           const int32_t* __restrict__ ids, int n_units,
-                                                           int log2_ppu, long long pool_units,
+                                                           const int32_t* __restrict__ ids, long long n_items,
+                                                           int log2_ipu, long long unit_bytes, long long pool_units,
                                                            uint32_t* __restrict__ sink) {
-  constexpr int DEPTH = 4;
+  constexpr int NL = TWO ? 2 * P : P;
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  const long long total = (long long)n_units << log2_ppu;
-  const long long per = (total + nw - 1) / nw;
-  const long long k0 = (long long)w * per;
-  const long long k1 = k0 + per < total ? k0 + per : total;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const long long nw = (long long)gridDim.x * 4;
+  const long long per = (n_items + nw - 1) / nw;
+  const long long i0 = (long long)w * per;
+  const long long i1 = i0 + per < n_items ? i0 + per : n_items;
   uint32_t acc = 0;
-  if (k0 < k1) {
-    const size_t ub = (size_t)1024 << log2_ppu;
-    long long wu = k0 >> log2_ppu;  // first unit of the id window
-    int win = wu + lane < n_units ? ids[wu + lane] : -1;
-    auto addr = [&](const char* base, long long k, int id) -> const char* {
-      return base + (size_t)id * ub + (size_t)(k & ((1 << log2_ppu) - 1)) * 1024 + lane * 16;
-    };
-    auto issue = [&](long long k, uint4 (&ra)[DEPTH], uint4 (&rb)[DEPTH]) {
+  if (i0 < i1) {
+    uint4 r[NL];
+    auto issue = [&](long long i) {
+      const int id = ((sconst_i32_gather*)ids)[i >> log2_ipu];
+      const long long uid = (unsigned long long)id < (unsigned long long)pool_units ? id : 0;
+      const size_t off = (size_t)uid * (size_t)unit_bytes + (size_t)(i & ((1 << log2_ipu) - 1)) * (P * 1024) +
+                         (size_t)lane * 16;
 #pragma unroll
-      for (int j = 0; j < DEPTH; ++j) {
-        const long long kk = k + j;
-        ra[j] = make_uint4(0, 0, 0, 0);
-        rb[j] = make_uint4(0, 0, 0, 0);
-        if (kk < k1) {
-          const long long u = kk >> log2_ppu;
-          if (u - wu >= 64) {  // slide the window (wave-uniform)
-            wu = u;
-            win = wu + lane < n_units ? ids[wu + lane] : -1;
-          }
-          const int id = __builtin_amdgcn_readlane(win, (int)(u - wu));
-          if ((unsigned long long)id < (unsigned long long)pool_units) {
-            ra[j] = gather_load(addr(pa, kk, id));
-            if (pb) rb[j] = gather_load(addr(pb, kk, id));
-          }
-        }
+      for (int p = 0; p < P; ++p) {
+        r[p] = gather_load(pa + off + p * 1024);
+        if constexpr (TWO) r[P + p] = gather_load(pb + off + p * 1024);
       }
     };
-    uint4 xa[DEPTH], xb[DEPTH], ya[DEPTH], yb[DEPTH];
-    issue(k0, xa, xb);
-    for (long long k = k0; k < k1; k += 2 * DEPTH) {
-      issue(k + DEPTH, ya, yb);
+    auto fold = [&]() {
 #pragma unroll
-      for (int j = 0; j < DEPTH; ++j) acc ^= xa[j].x ^ xa[j].y ^ xa[j].z ^ xa[j].w ^ xb[j].x ^ xb[j].y ^ xb[j].z ^ xb[j].w;
-      if (k + DEPTH >= k1) break;
-      issue(k + 2 * DEPTH, xa, xb);
-#pragma unroll
-      for (int j = 0; j < DEPTH; ++j) acc ^= ya[j].x ^ ya[j].y ^ ya[j].z ^ ya[j].w ^ yb[j].x ^ yb[j].y ^ yb[j].z ^ yb[j].w;
+      for (int p = 0; p < NL; ++p) acc ^= r[p].x ^ r[p].y ^ r[p].z ^ r[p].w;
+    };
+    issue(i0);
+    for (long long i = i0 + 1; i < i1; ++i) {
+      fold();
+      __builtin_amdgcn_sched_barrier(0);  // fold, then issue: the order that keeps one item in flight
+      issue(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    fold();
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) acc ^= __shfl_xor(acc, m);
@@ -221,11 +216,29 @@ int launch_gather_units(const void* pool_a, const void* pool_b, const int32_t* i
                         long long pool_units, void* sink, int sink_words, hipStream_t stream) {
   int l = 0;
   while ((1 << l) < unit_kib) ++l;
+  const int P = unit_kib < 4 ? unit_kib : 4;
+  const int log2_ipu = unit_kib < 4 ? 0 : l - 2;
+  const long long n_items = (long long)n_units << log2_ipu;
+  const long long unit_bytes = (long long)unit_kib * 1024;
   const DeviceInfo& dev = device_info();
-  const long long waves = std::min<long long>((long long)std::max(dev.num_cus, 1) * 6 * 4, sink_words);
+  const long long waves = std::min<long long>((long long)std::max(dev.num_cus, 1) * 8, sink_words);
   const int grid = (int)std::max<long long>(waves / 4, 1);
-  hipLaunchKernelGGL(gather_units_kernel, dim3(grid), dim3(256), 0, stream, (const char*)pool_a,
-                     (const char*)pool_b, ids, n_units, l, pool_units, (uint32_t*)sink);
+  const char* a = (const char*)pool_a;
+  const char* b = (const char*)pool_b;
+  uint32_t* sk = (uint32_t*)sink;
+#define PKV_GATHER(PP)                                                                                        \
+  if (P == PP) {                                                                                              \
+    if (b)                                                                                                    \
+      hipLaunchKernelGGL((gather_units_kernel<PP, true>), dim3(grid), dim3(256), 0, stream, a, b, ids, n_items, \
+                         log2_ipu, unit_bytes, pool_units, sk);                                              \
+    else                                                                                                      \
+      hipLaunchKernelGGL((gather_units_kernel<PP, false>), dim3(grid), dim3(256), 0, stream, a, b, ids,        \
+                         n_items, log2_ipu, unit_bytes, pool_units, sk);                                     \
+  }
+  PKV_GATHER(1)
+  PKV_GATHER(2)
+  PKV_GATHER(4)
+#undef PKV_GATHER
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -451,14 +451,25 @@ __device__ __forceinline__ int chunks_of(int ctx, int maxctx, int nt, int window
   return (ctx + nt - 1) / nt - lo / nt;
 }
 
+// Context lengths of batches up to this size are kept in LDS by every
+// wavefront after its first read, so that later look-ups (the sequence
+// holding the share's first chunk, the next unit) cost no memory round trip.
+constexpr int kCtxCache = 512;
+
+// Context length of sequence s, clamped to the table's capacity.
+__device__ __forceinline__ int ctx_of(const DecodeArgs& a, const int* lc, int maxctx, int s) {
+  return a.S <= kCtxCache ? lc[s] : min(a.ctx_lens[s], maxctx);
+}
+
 // Next non-empty unit after (h, s) in kv-head-major order; false at the end.
-__device__ __forceinline__ bool next_unit(const DecodeArgs& a, int maxctx, int& h, int& s, int& ctx) {
+__device__ __forceinline__ bool next_unit(const DecodeArgs& a, const int* lc, int maxctx, int& h, int& s,
+                                          int& ctx) {
   for (;;) {
     if (++s == a.S) {
       s = 0;
       if (++h == a.Hkv) return false;
     }
-    ctx = min(a.ctx_lens[s], maxctx);
+    ctx = ctx_of(a, lc, maxctx, s);
     if (ctx > 0) return true;
   }
 }
@@ -468,6 +479,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   using SH = DShape<T, D, G>;
   constexpr int E = SH::E;
   __shared__ __attribute__((aligned(16))) float lds[kWavesPerWG][SH::LDS_FLOATS];
+  __shared__ int lds_ctx[kWavesPerWG][kCtxCache];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   int wg = blockIdx.x;
@@ -478,28 +490,19 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
   const int w = wg * kWavesPerWG + wid;
   float* L = lds[wid];
+  int* lc = lds_ctx[wid];
   constexpr int NT = SH::NT;
   const int maxctx = a.max_blocks << a.log2B;
   const int S = a.S;
   if (w >= a.nW) return;
   if (lane == 0) a.jobs[w] = make_int2(-1, 0);
 
-  // zero the outputs of empty sequences
-  for (int s = w; s < S; s += a.nW) {
-    if (a.ctx_lens[s] <= 0) {
-      const size_t n = (size_t)a.Hq * D;
-      for (size_t i = lane; i < n; i += 64) {
-        float z = 0.f;
-        store_out<T>(a.out, (size_t)s * n + i, &z, 1);
-      }
-    }
-  }
-
-  // Chunks per kv head, and this wavefront's share [gstart, gend), in two
-  // round trips whatever the batch size: lane l first sums the chunks of
-  // its own contiguous segment of sequences (all of its loads in flight at
-  // once), a scan over the 64 segments finds the one holding chunk gstart,
-  // and one more load of that segment finds the sequence.
+  // Chunks per kv head, and this wavefront's share [gstart, gend), in one
+  // round trip whatever the batch size: lane l sums the chunks of its own
+  // contiguous segment of sequences (all of its loads in flight at once),
+  // and a scan over the 64 segments finds the one holding chunk gstart.
+  // Batches up to kCtxCache sequences (segments of at most 8) keep every
+  // length in LDS; longer segments are walked again from memory.
   const int seg = (S + 63) / 64;  // sequences per lane segment
   const int sbeg = min(lane * seg, S), send = min(sbeg + seg, S);
   int my_n = 0;
@@ -508,8 +511,24 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) cx[j] = si + j < send ? a.ctx_lens[si + j] : 0;  // all eight loads in flight
 #pragma unroll
-    for (int j = 0; j < 8; ++j) my_n += chunks_of(cx[j], maxctx, NT, a.window);
+    for (int j = 0; j < 8; ++j) {
+      my_n += chunks_of(cx[j], maxctx, NT, a.window);
+      if (S <= kCtxCache && si + j < send) lc[si + j] = min(cx[j], maxctx);
+    }
   }
+  if (S <= kCtxCache) wave_lds_sync();
+
+  // zero the outputs of empty sequences
+  for (int s = w; s < S; s += a.nW) {
+    if (ctx_of(a, lc, maxctx, s) <= 0) {
+      const size_t n = (size_t)a.Hq * D;
+      for (size_t i = lane; i < n; i += 64) {
+        float z = 0.f;
+        store_out<T>(a.out, (size_t)s * n + i, &z, 1);
+      }
+    }
+  }
+
   const int seg_incl = wave_incl_scan_i(my_n, lane);
   const int W1 = __builtin_amdgcn_readlane(seg_incl, 63);
   const int Wtot = a.Hkv * W1;
@@ -526,22 +545,35 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     if (!seg_hit) return;  // context lengths changed under the kernel: do nothing
     const int ls = __ffsll((long long)seg_hit) - 1;  // lane whose segment holds it
     const int base = ls * seg;
+    const int bend = min(base + seg, S);
     P = __builtin_amdgcn_readlane(seg_incl - my_n, ls);
-    // the segment (at most 64 sequences for batches up to 4,096; longer
-    // segments are walked 64 at a time)
     bool found = false;
-    for (int b0 = base; b0 < min(base + seg, S) && !found; b0 += 64) {
-      const int si = b0 + lane;
-      const int n = si < min(base + seg, S) ? chunks_of(a.ctx_lens[si], maxctx, NT, a.window) : 0;
-      const int incl = wave_incl_scan_i(n, lane);
-      const unsigned long long hit = __ballot(P + incl > rem);
-      if (hit) {
-        const int first = __ffsll((long long)hit) - 1;
-        s = b0 + first;
-        P += __builtin_amdgcn_readlane(incl - n, first);
-        found = true;
-      } else {
-        P += __builtin_amdgcn_readlane(incl, 63);
+    if (S <= kCtxCache) {
+      // the segment's lengths are in LDS (at most 8)
+      for (int si = base; si < bend && !found; ++si) {
+        const int n = chunks_of(lc[si], maxctx, NT, a.window);
+        if (P + n > rem) {
+          s = si;
+          found = true;
+        } else {
+          P += n;
+        }
+      }
+    } else {
+      // walked 64 sequences at a time
+      for (int b0 = base; b0 < bend && !found; b0 += 64) {
+        const int si = b0 + lane;
+        const int n = si < bend ? chunks_of(a.ctx_lens[si], maxctx, NT, a.window) : 0;
+        const int incl = wave_incl_scan_i(n, lane);
+        const unsigned long long hit = __ballot(P + incl > rem);
+        if (hit) {
+          const int first = __ffsll((long long)hit) - 1;
+          s = b0 + first;
+          P += __builtin_amdgcn_readlane(incl - n, first);
+          found = true;
+        } else {
+          P += __builtin_amdgcn_readlane(incl, 63);
+        }
       }
     }
     if (!found) return;
@@ -549,12 +581,12 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
 
   Unit<T, D, G> cur, nxt;
   int c = rem - P;  // chunk of `cur` being computed
-  open_unit(cur, a, h, s, min(a.ctx_lens[s], maxctx), gstart - c, c, lane);
+  open_unit(cur, a, h, s, ctx_of(a, lc, maxctx, s), gstart - c, c, lane);
   int seg_c0 = c;  // first chunk of cur in this wavefront's share
   bool have_next = false;
   {
     int h2 = h, s2 = s, ctx2 = 0;
-    if (cur.g0 + cur.n < gend && next_unit(a, maxctx, h2, s2, ctx2)) {
+    if (cur.g0 + cur.n < gend && next_unit(a, lc, maxctx, h2, s2, ctx2)) {
       open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
       have_next = true;
     }
@@ -587,7 +619,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     seg_c0 = 0;
     have_next = false;
     int h2 = cur.h, s2 = cur.s, ctx2 = 0;
-    if (cur.g0 + cur.n < gend && next_unit(a, maxctx, h2, s2, ctx2)) {
+    if (cur.g0 + cur.n < gend && next_unit(a, lc, maxctx, h2, s2, ctx2)) {
       open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
       have_next = true;
     }
