@@ -134,8 +134,13 @@ __device__ __forceinline__ void tile_barrier() {
 // Written as assembly so that the compiler's wait-count pass, which cannot
 // tell which LDS buffer such a transfer writes, adds no wait for it before
 // every LDS read; tile_barrier waits for the transfers explicitly.
-__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+// The LDS destination is an LDS byte address (lds_addr of an LDS array),
+// which stays a 32-bit constant: a generic pointer would be carried in a
+// register pair and converted at every transfer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void_t*)p; }
+
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
@@ -147,8 +152,8 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
 
 // The same transfer with a wavefront-uniform 64-bit base in SGPRs and a
 // 32-bit per-lane byte offset (the instruction's saddr form).
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint8_t* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
@@ -171,7 +176,7 @@ __device__ __forceinline__ int table_entry(const int32_t* trow, int i) { return 
 // holds.
 template <int D>
 __device__ __forceinline__ void dma_lanes(const PrefillArgs& a, const int32_t* trow, int kvh, int t0, int ctx, int g,
-                                          int lane, uint8_t* kdst, uint8_t* vdst) {
+                                          int lane, uint32_t kdst, uint32_t vdst) {
   using PS = PShape<D>;
   const int sl = g * 64 + lane;  // 16-byte slot
   const int key = sl / PS::PIECES;
@@ -238,7 +243,7 @@ __device__ __forceinline__ TileEntries<D> tile_entries(const PrefillArgs& a, con
 template <int D>
 __device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int32_t* trow, const TileEntries<D>& ent,
                                          int kvh, int t0, int ctx, int wave, int lane, const uint32_t* voff,
-                                         uint8_t* kdst, uint8_t* vdst) {
+                                         uint32_t kdst, uint32_t vdst) {
   using PS = PShape<D>;
   constexpr int KPX = 64 / PS::PIECES;  // keys per transfer
   const bool whole = t0 + kPKT <= ctx;
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   TileEntries<D> ent;  // block ids of tile td of di
   auto entries = [&]() __attribute__((always_inline)) { return tile_entries<D>(a, di.trow, td * kPKT, wave); };
   auto dma_next = [&](auto r) __attribute__((always_inline)) {
-    dma_tile<D>(a, di.trow, ent, di.kvh, td * kPKT, di.ctx, wave, lane, voff, kbuf(r), vbuf(r));
+    dma_tile<D>(a, di.trow, ent, di.kvh, td * kPKT, di.ctx, wave, lane, voff, lds_addr(kbuf(r)), lds_addr(vbuf(r)));
     if (++td == di.n_tiles) {
       di = item_at(di.k + 1);
       td = 0;
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       const int p = (sl % PS::PIECES) ^ swz<D>(r);
       const int row = min(it.q0 + wave * 32 + r, it.C - 1);
       lds_dma16((const uint8_t*)a.q + ((size_t)(it.qbeg + row) * a.Hq + it.h) * PS::ROWB + p * 16,
-                qb + wave * 32 * PS::ROWB + x * 1024);
+                lds_addr(qb) + (uint32_t)(wave * 32 * PS::ROWB + x * 1024));
     }
   };
   auto live = [&](int j) __attribute__((always_inline)) { return wave_live && j * kPKT <= wave_last_pos; };
