@@ -16,9 +16,8 @@
 //
 // Per pair of tiles and wavefront (16 rows x 32 keys):
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head dims of
-//                 K, straight from global memory (lane l: key l % 16, dims
-//                 8 (l / 16) .. + 7 of each 32-wide step), B = the stacked
-//                 query rows.  The accumulator gives lane l row l % 16 and
+//                 K (lane l: key l % 16, dims 8 (l / 16) .. + 7 of each
+//                 32-wide step), B = the stacked query rows.  The accumulator gives lane l row l % 16 and
 //                 keys 4 (l / 16) .. + 3, so a row's softmax state lives in
 //                 the four lanes l % 16 + 16 j.
 //   O^T += V^T P^T  the same instruction, A = V^T (16 head dims x the 32
@@ -28,6 +27,11 @@
 //                 any order, so the pair's keys are assigned to k as the
 //                 accumulators hold them: k = 8 (l / 16) + e is key
 //                 4 (l / 16) + e % 4 of tile e / 4.
+// K and V are read from global memory 1 KiB of a tile per instruction
+// (lane l: the 16 bytes at 16 l), whole cache lines at a time, and pass
+// through swizzled LDS into the operand layouts above: loading the operand
+// layout directly reads half a cache line of each of 16 keys per
+// instruction, and streams about a fifth slower.
 // Online softmax with the lazy reference max of the plain decode (weights
 // below 2^8), fp32 accumulation; the eight wavefronts' partials are merged
 // in LDS with their log-sum-exp weights at the end.
@@ -82,20 +86,25 @@ __device__ __forceinline__ uint32_t pack2_bf16_rne(float a, float b) {
 // A tile of the list: 16 keys of one block, the member whose rows attend it
 // (-1: every member), and how many of its keys exist.
 struct Tile {
-  int blk;    // physical block (may be outside the pool: those keys read as NaN for their rows)
-  int key0;   // first key's slot inside the block
-  int owner;  // member index, or -1 for a shared tile
-  int valid;  // keys 0 .. valid - 1 exist (0: no tile)
+  long long row0;  // first key's row in the pool ([block][kv head][slot]); 0 when nothing is read
+  int owner;       // member index, or -1 for a shared tile
+  int valid;       // keys 0 .. valid - 1 exist (0: no tile, or its block is outside the pool)
+  int bad;         // the block lies outside the pool: the attending rows' results are NaN
 };
 
 template <int D>
 __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
   static_assert(D == 128, "stacked decode: head_dim 128");
   constexpr int ROWB = D * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kSW][2][16 * ROWB];  // V tiles of the current pair
-  __shared__ __attribute__((aligned(16))) float part[kSW][kRows][D + 2];  // partials for the final merge
+  constexpr int TB = 16 * ROWB;  // bytes of one tile
+  // Per wavefront: K0, K1, V0, V1 of the pair being computed (swizzled
+  // rows); at the end the same bytes hold the wavefront's partial for the
+  // merge (kRows x (D + 2) floats).
+  __shared__ __attribute__((aligned(16))) uint8_t wb[kSW][4 * TB];
+  static_assert(kRows * (D + 2) * 4 <= 4 * TB, "the partial fits the tile buffers");
+  auto partw = [&](int w8) { return (float(*)[D + 2])(void*)wb[w8]; };
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar table reads
   const int gi = blockIdx.x / a.Hkv;
   const int h = blockIdx.x - gi * a.Hkv;
   const int B = 1 << a.log2B;
@@ -126,27 +135,34 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
   // tile t of the list
   auto tile_at = [&](int t) -> Tile {
     Tile r;
-    r.valid = 0;
-    r.blk = -1;
-    r.key0 = 0;
+    r.row0 = 0;
     r.owner = -1;
+    r.valid = 0;
+    r.bad = 0;
     if (t >= ntiles) return r;
+    int blk, key0;
     if (t < sbt) {
-      r.blk = ((sconst_i32_t*)trow0)[t / tiles_per_block];
-      r.key0 = (t % tiles_per_block) * 16;
+      blk = ((sconst_i32_t*)trow0)[t / tiles_per_block];
+      key0 = (t % tiles_per_block) * 16;
       r.valid = 16;
-      return r;
+    } else {
+      const int tp = t - sbt;
+      const unsigned long long hit = __ballot(incl > tp);
+      const int m = __ffsll((long long)hit) - 1;
+      const int before = __builtin_amdgcn_readlane(incl - my_priv, m);
+      const int ctx = __builtin_amdgcn_readlane(my_ctx, m);
+      const int tok = sb * B + (tp - before) * 16;  // first key of the tile
+      r.owner = m;
+      blk = ((sconst_i32_t*)(a.tables + (size_t)(g0 + m) * a.max_blocks))[tok >> a.log2B];
+      key0 = tok & (B - 1);
+      r.valid = min(16, ctx - tok);
     }
-    const int tp = t - sbt;
-    const unsigned long long hit = __ballot(incl > tp);
-    const int m = __ffsll((long long)hit) - 1;
-    const int before = __builtin_amdgcn_readlane(incl - my_priv, m);
-    const int ctx = __builtin_amdgcn_readlane(my_ctx, m);
-    const int tok = sb * B + (tp - before) * 16;  // first key of the tile
-    r.owner = m;
-    r.blk = ((sconst_i32_t*)(a.tables + (size_t)(g0 + m) * a.max_blocks))[tok >> a.log2B];
-    r.key0 = tok & (B - 1);
-    r.valid = min(16, ctx - tok);
+    if ((unsigned)blk < (unsigned)a.num_blocks) {
+      r.row0 = (((long long)blk * a.Hkv + h) << a.log2B) + key0;
+    } else {
+      r.bad = 1;
+      r.valid = 0;  // nothing of it is read
+    }
     return r;
   };
 
@@ -164,23 +180,21 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
       qf[s] = row_live ? *(const uint4*)(qp + 32 * s + 8 * grp) : make_uint4(0, 0, 0, 0);
   }
 
-  // per-lane K/V loads of a tile: key l % 16, dims 32 s + 8 (l / 16)
+  // K/V loads of a tile: instruction s reads 1 KiB, lane l the 16 bytes at
+  // 1 KiB s + 16 l (key 4 s + l / 16, dims 8 (l % 16) .. + 7).  The loads
+  // are unconditional (a missing tile reads row0 = 0 and is never used), so
+  // that no load result is merged with a zero before use: keys past a
+  // tile's end are masked in the scores and zeroed where V is staged.
   struct TileData {
     uint4 k[D / 32];
     uint4 v[D / 32];
-    int bad;
   };
-  const size_t kvh = (size_t)h << a.log2B;  // rows before this kv head inside a block
   auto load_tile = [&](const Tile& t, TileData& d) {
-    const bool in_pool = (unsigned)t.blk < (unsigned)a.num_blocks;
-    d.bad = t.valid > 0 && !in_pool;
-    const bool key_ok = in_pool && row < t.valid;
-    const size_t rowi = ((size_t)t.blk * a.Hkv << a.log2B) + kvh + t.key0 + row;
-    const size_t off = rowi * D + 8 * grp;
+    const size_t off = (size_t)t.row0 * D + 8 * lane;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      d.k[s] = key_ok ? sload_stream(a.k_cache + off + 32 * s) : make_uint4(0, 0, 0, 0);
-      d.v[s] = key_ok ? sload_stream(a.v_cache + off + 32 * s) : make_uint4(0, 0, 0, 0);
+      d.k[s] = sload_stream(a.k_cache + off + 512 * s);
+      d.v[s] = sload_stream(a.v_cache + off + 512 * s);
     }
   };
 
@@ -192,21 +206,25 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
 
   // S^T of one tile, masked: -inf for keys past the tile's end and for rows
   // of other members; lane keeps keys 4 grp .. 4 grp + 3 of row `row`.
-  auto scores = [&](const Tile& t, const TileData& d, float (&sc)[4]) {
+  auto scores = [&](const Tile& t, int which, float (&sc)[4]) {
+    const uint8_t* kb = wb[wid] + which * TB;
+    uint4 kf[D / 32];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) kf[s] = *(const uint4*)(kb + vslot(row, 4 * s + grp) * 16);
     sf32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sbf16x8_t, d.k[s]),
+      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sbf16x8_t, kf[s]),
                                                    __builtin_bit_cast(sbf16x8_t, qf[s]), s4, 0, 0, 0);
     const bool row_on = row_live && (t.owner < 0 || t.owner == row_member);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (row_on && 4 * grp + r < t.valid) ? s4[r] * c : -INFINITY;
   };
 
-  // O^T += V^T P^T over the pair held in vt[wid]: for each 16-dim tile, two
+  // O^T += V^T P^T over the pair's V in LDS: for each 16-dim tile, two
   // transposing reads (keys 4 grp .. + 3 of each tile, dim 16 dt + l % 16).
   auto pv = [&](const sbf16x8_t& pb) {
-    const uint8_t* base = vt[wid][0];
+    const uint8_t* base = wb[wid] + 2 * TB;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const int key = 4 * grp + (row >> 2);   // lane i of the 16-lane group names key 4 grp + i / 4
@@ -221,20 +239,26 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
     }
   };
 
-  // V of a tile into the wavefront's LDS buffer (row-major, swizzled)
-  auto stage_v = [&](const TileData& d, int which) {
-    uint8_t* base = vt[wid][which];
+  // K and V of a tile into the wavefront's LDS buffers (row-major,
+  // swizzled).  V rows past the tile's end become zeros: their weights are
+  // zero, and 0 x NaN would not be.
+  auto stage = [&](const Tile& t, const TileData& d, int which) {
+    uint8_t* kb = wb[wid] + which * TB;
+    uint8_t* vb = wb[wid] + (2 + which) * TB;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) *(uint4*)(base + vslot(row, 4 * s + grp) * 16) = d.v[s];
+    for (int s = 0; s < D / 32; ++s) {
+      const int key = 4 * s + grp;
+      const int slot = vslot(key, row) * 16;
+      *(uint4*)(kb + slot) = d.k[s];
+      *(uint4*)(vb + slot) = key < t.valid ? d.v[s] : make_uint4(0, 0, 0, 0);
+    }
   };
 
-  // One pair of tiles: scores, online softmax, weighted V sum.
-  auto step = [&](const Tile& t0, const TileData& d0, const Tile& t1, const TileData& d1) {
-    stage_v(d0, 0);
-    stage_v(d1, 1);
+  // One pair of tiles, staged in LDS: scores, online softmax, weighted V sum.
+  auto step = [&](const Tile& t0, const Tile& t1) {
     float s0[4], s1[4];
-    scores(t0, d0, s0);
-    scores(t1, d1, s1);
+    scores(t0, 0, s0);
+    scores(t1, 1, s1);
     float cmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
     cmax = fmaxf(cmax, xor_lane<16>(cmax));
     cmax = fmaxf(cmax, xor_lane<32>(cmax));
@@ -266,55 +290,61 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
     ps = dot2_bf16(pw.w, 0x3f803f80u, ps);
     const bool row_on0 = row_live && (t0.owner < 0 || t0.owner == row_member);
     const bool row_on1 = row_live && (t1.owner < 0 || t1.owner == row_member);
-    l_run += ps + (((d0.bad && row_on0) || (d1.bad && row_on1)) ? __builtin_nanf("") : 0.f);
+    l_run += ps + (((t0.bad && row_on0) || (t1.bad && row_on1)) ? __builtin_nanf("") : 0.f);
     wave_lds_sync();
     pv(__builtin_bit_cast(sbf16x8_t, pw));
     wave_lds_sync();  // the next pair's V overwrites the buffers
   };
 
   // Wavefront wid takes pairs wid, wid + kSW, ...: tiles 2 p and 2 p + 1.
-  // The K/V loads of the next pair are in flight while a pair is computed,
-  // and the table entries of the pair after that are read (through the
-  // scalar cache) one step ahead of its loads.
+  // A step stages pair c (the one computed) in LDS, which frees its
+  // registers, issues the loads of pair x (the next one) and computes pair
+  // c while they are in flight; the table entries of the pair after x are
+  // read (through the scalar cache) in the same step.  The two register
+  // sets swap roles every step, so no load result is ever copied.  The
+  // loads of x are issued past the end too (a missing tile reads row0 = 0):
+  // a load issued on one path only would make the compiler's wait counts
+  // assume the worst for every load.
   const int npairs = (ntiles + 1) / 2;
-  int pi = wid;
-  if (pi < npairs) {
-    Tile ta = tile_at(2 * pi), tb = tile_at(2 * pi + 1);
-    Tile tc = tile_at(2 * (pi + kSW)), td = tile_at(2 * (pi + kSW) + 1);
-    TileData da, db;
-    load_tile(ta, da);
-    load_tile(tb, db);
-    for (;;) {
-      const bool more = pi + kSW < npairs;
-      TileData dc, dd;
-      Tile te, tf;
-      if (more) {
-        load_tile(tc, dc);
-        load_tile(td, dd);
-        te = tile_at(2 * (pi + 2 * kSW));
-        tf = tile_at(2 * (pi + 2 * kSW) + 1);
-      }
-      step(ta, da, tb, db);
-      if (!more) break;
-      ta = tc;
-      tb = td;
-      tc = te;
-      td = tf;
-      da = dc;
-      db = dd;
+  if (wid < npairs) {
+    int pi = wid;
+    Tile c0 = tile_at(2 * pi), c1 = tile_at(2 * pi + 1);
+    Tile x0 = tile_at(2 * (pi + kSW)), x1 = tile_at(2 * (pi + kSW) + 1);
+    TileData bufA[2], bufB[2];
+    load_tile(c0, bufA[0]);
+    load_tile(c1, bufA[1]);
+    auto pair_step = [&](TileData (&cb)[2], TileData (&nb)[2]) -> bool {
+      stage(c0, cb[0], 0);
+      stage(c1, cb[1], 1);
+      wave_lds_sync();
+      load_tile(x0, nb[0]);
+      load_tile(x1, nb[1]);
+      const Tile y0 = tile_at(2 * (pi + 2 * kSW)), y1 = tile_at(2 * (pi + 2 * kSW) + 1);
+      step(c0, c1);
       pi += kSW;
+      c0 = x0;
+      c1 = x1;
+      x0 = y0;
+      x1 = y1;
+      return pi < npairs;
+    };
+    for (;;) {
+      if (!pair_step(bufA, bufB)) break;
+      if (!pair_step(bufB, bufA)) break;
     }
   }
 
-  // this wavefront's partial: lane l writes row l % 16, dims 16 dt + 4 grp .. + 3
+  // this wavefront's partial (over its own tile buffers): lane l writes row
+  // l % 16, dims 16 dt + 4 grp .. + 3
   float lsum = l_run + xor_lane<16>(l_run);
   lsum += xor_lane<32>(lsum);
+  float(*pw)[D + 2] = partw(wid);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    *(float4*)&part[wid][row][16 * dt + 4 * grp] = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    *(float4*)&pw[row][16 * dt + 4 * grp] = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
   if (grp == 0) {
-    part[wid][row][D] = m_run;
-    part[wid][row][D + 1] = lsum;
+    pw[row][D] = m_run;
+    pw[row][D + 1] = lsum;
   }
   __syncthreads();
 
@@ -327,14 +357,14 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
     if (r < kRows && mb < nm) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kSW; ++w) M = fmaxf(M, part[w][r][D]);
+      for (int w = 0; w < kSW; ++w) M = fmaxf(M, partw(w)[r][D]);
       float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < kSW; ++w) {
-        const float mw = part[w][r][D];
+        const float mw = partw(w)[r][D];
         const float ww = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        L = fmaf(ww, part[w][r][D + 1], L);
-        const float4 x = *(const float4*)&part[w][r][d0];
+        L = fmaf(ww, partw(w)[r][D + 1], L);
+        const float4 x = *(const float4*)&partw(w)[r][d0];
         o[0] = fmaf(ww, x.x, o[0]);
         o[1] = fmaf(ww, x.y, o[1]);
         o[2] = fmaf(ww, x.z, o[2]);

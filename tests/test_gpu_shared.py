@@ -156,3 +156,25 @@ def test_shared_matches_plain_decode():
     diff = (out.float() - ref.float()).abs().max().item()
     say(f"[gpu] shared vs plain decode: max diff {diff:.3g}")
     assert diff <= BF16_TOL
+
+
+def test_many_small_groups():
+    """600 one-member groups of 1 .. 40 tokens (1 .. 3 tiles each): most
+    wavefronts have no pair at all, tiles end inside themselves."""
+    rng = np.random.default_rng(76)
+    lens = [int(x) for x in rng.integers(1, 41, size=600)]
+    wl = W.decode_workload("sp-small", 76, lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                           num_blocks=2048, dtype="bf16")
+    check(wl)
+
+
+def test_long_prompt_and_single_short_sequences():
+    """One prompt of 6,000 tokens with 4 branches (47 pairs per wavefront);
+    single sequences of 5 and 100 tokens."""
+    wl = W.shared_prefix(77, num_prompts=1, prompt_len=6000, n_branches=4, priv_hi=40, num_blocks=2048,
+                         fork_lo=5990, fork_hi=5999, name="sp-long")
+    check(wl)
+    for n in (5, 100):
+        wl = W.decode_workload(f"sp-tiny{n}", 78, [n], num_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, num_blocks=16, dtype="bf16")
+        check(wl)
