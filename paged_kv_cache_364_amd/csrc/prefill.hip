@@ -617,9 +617,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   };
 
   // Tiles go from global memory straight into LDS, three buffers deep:
-  // step j issues the transfers of tile j + 2, computes tile j, then waits
-  // for its own share of tile j + 1 (issued one step earlier) and meets the
-  // other wavefronts at the barrier, after which tile j + 1 is whole.
+  // step j computes tile j, issuing the transfers of tile j + 2 between its
+  // softmax and its V products, then waits for its own share of tile j + 1
+  // (issued one step earlier) and meets the other wavefronts at the
+  // barrier, after which tile j + 1 is whole.
   // Tile j + 2 goes over tile j - 1, which every wavefront finished before
   // the previous barrier.
   // Output of item ci: the accumulated rows over their sums.
@@ -658,22 +659,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     l_run = 0.f;
   };
 
-  // One step of the stream: transfer the tile two ahead (kept in buffer
-  // r + 2 mod 3, which held the tile computed two steps ago), compute tile
-  // tc of ci from buffer r, then wait for this wavefront's share of the
+  // One step of the stream: compute tile tc of ci from buffer r, transfer
+  // the tile two ahead (kept in buffer r + 2 mod 3, which held the tile
+  // computed two steps ago), then wait for this wavefront's share of the
   // next tile and meet the others at the barrier.  On the last tile of an
   // item the next item's query rows go into LDS once this wavefront has
-  // read its own (after its S^T products); the barrier then waits for them
-  // too.  Returns false after the last item.
-  bool q_wait = false;  // the query rows of ci may still be on their way
+  // read its own (after its S^T products), ahead of the tile transfers; the
+  // next step waits for them before its S^T products.  Returns false after
+  // the last item.
+  bool q_wait = false;   // the query rows of ci may still be on their way
+  bool q_newer = false;  // and the previous step's tile transfers went out after them
   auto step = [&](auto r) __attribute__((always_inline)) {
     constexpr int R = decltype(r)::value;
     constexpr int NT = 2 * PS::DMA_PER_WAVE;  // transfers of one tile per wavefront
     const bool more = di.k >= 0;
-    if (more) dma_next(std::integral_constant<int, (R + 2) % 3>{});
     if (q_wait) {
-      // the query rows went out before this step's tile transfers
-      if (more)
+      if (q_newer)
         __builtin_amdgcn_s_waitcnt((NT & 15) | ((NT >> 4) << 14) | (7 << 4) | (15 << 8));
       else
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -687,10 +688,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's query reads are done
       q_dma(nci);
     }
-    if (lv) {
-      sm_phase(tc);
-      o_phase(r);
-    }
+    if (lv) sm_phase(tc);
+    // The tile two ahead goes out after the softmax, while the matrix cores
+    // still work on S^T and before the V products: issued at the start of
+    // the step, the transfers held up the products (measured 4% slower).
+    if (more) dma_next(std::integral_constant<int, (R + 2) % 3>{});
+    if (lv) o_phase(r);
+    q_newer = more;
     if (q_next) {
       if (more)
         tile_barrier<NT + QX>();
