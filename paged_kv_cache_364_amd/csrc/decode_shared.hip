@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * kSW) void decode_shared_kernel(SharedArgs a) {
   sb = min(max(sb, 0), a.max_blocks);
   // lane m < nm: member m's context and private tiles
   const int my_ctx = lane < nm ? min(a.ctx_lens[g0 + lane], maxctx) : 0;
-  const int sbt = sb * tiles_per_block;  // shared tiles
+  const int sbt = nm > 0 ? sb * tiles_per_block : 0;  // shared tiles (none for a group with no member)
   const int my_priv = lane < nm ? max(0, (my_ctx - sb * B + 15) >> 4) : 0;
   int incl = my_priv;
 #pragma unroll
