@@ -2,10 +2,12 @@
 paged prefill leg (OPT-13B shape).
 
 Decode step = the device work of one decode step of one layer for the whole
-batch: ``kv_write`` of the 64 new tokens into their slots, then
-``paged_attention_decode`` (main pass + log-sum-exp merge) over the paged
-cache.  Block tables and slot mappings come from the C++ block allocator and
-are resident on the device before timing starts.  Layers rotate over
+batch: the 64 new tokens' K/V written into their slots and the decode (main
+pass + log-sum-exp merge) over the paged cache, issued as one call,
+``paged_attention_decode_append``, whose results are bit for bit those of
+``kv_write`` then ``paged_attention_decode``; the two-call step is timed
+too and reported beside it.  Block tables and slot mappings come from the
+C++ block allocator and are resident on the device before timing starts.  Layers rotate over
 separate per-layer pools (32 x 25,600 blocks = 50 GiB) so the 256 MB
 Infinity Cache cannot hold the working set.
 
@@ -561,6 +563,11 @@ def main():
     if args.calibrate_copy_mib > 0:
         calibration_copy(torch, api, dev, args.calibrate_copy_mib)
 
+    def append_decode(i):
+        li = i % L
+        api.paged_attention_decode_append(out, q, kn, vn, kps[li], vps[li], st.tables_dev, st.lens_dev, scale,
+                                          workspace=ws)
+
     def decode(i):
         li = i % L
         api.paged_attention_decode(out, q, kps[li], vps[li], st.tables_dev, st.lens_dev, scale, workspace=ws)
@@ -569,9 +576,14 @@ def main():
         li = i % L
         api.kv_write(kn, vn, slots, kps[li], vps[li])
 
-    def step(i):
+    def two_calls(i):
         write(i)
         decode(i)
+
+    # the step: each sequence's new token written through its block table and
+    # the decode over the whole context, in one call (bitwise the same as
+    # kv_write then paged_attention_decode)
+    step = append_decode
 
     for i in range(args.warmup):
         step(i)
@@ -586,19 +598,33 @@ def main():
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_per_step = t_total * 1e3 / K
-    # per-call durations: K decode calls (then K kv_write calls) back to back
-    # between one pair of events on the kernels' stream
-    dec_avg, dec_ms = timed_calls(torch, decode, K, 5, stream)
+    # the same step as two calls, timed the same way
+    for i in range(args.warmup):
+        two_calls(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        two_calls(args.warmup + i)
+    torch.cuda.synchronize()
+    ms_two = (time.perf_counter() - t_start) * 1e3 / K
+    # per-call durations: K calls back to back between one pair of events on
+    # the kernels' stream (the step's call, then the plain decode, then
+    # kv_write)
+    dec_avg, dec_ms = timed_calls(torch, append_decode, K, 5, stream)
     dec_ms = np.array(dec_ms)
+    plain_avg, _ = timed_calls(torch, decode, K, 5, stream, per_call=False)
     kvw_avg, _ = timed_calls(torch, write, K, 5, stream, per_call=False)
-    log(f"decode avg {dec_avg * 1e3:.1f} us (per-call events: median {np.median(dec_ms) * 1e3:.1f}, "
+    log(f"append+decode avg {dec_avg * 1e3:.1f} us (per-call events: median {np.median(dec_ms) * 1e3:.1f}, "
         f"p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
-        f"kv_write avg {kvw_avg * 1e3:.1f} us; wall {ms_per_step * 1e3:.1f} us/step")
+        f"plain decode avg {plain_avg * 1e3:.1f} us; kv_write avg {kvw_avg * 1e3:.1f} us; "
+        f"wall {ms_per_step * 1e3:.1f} us/step ({ms_two * 1e3:.1f} as two calls)")
 
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = (kv_bytes + qo_bytes) / (dec_avg * 1e-3) / 1e9
+    new_bytes = 2 * S * Hkv * D * 2 * 2  # the new rows read and stored, K and V
+    achieved = (kv_bytes + qo_bytes + new_bytes) / (dec_avg * 1e-3) / 1e9
+    plain_achieved = (kv_bytes + qo_bytes) / (plain_avg * 1e-3) / 1e9
     tb = profiling.traffic_bytes(profiling.read_traffic(TRAFFIC_FILE),
-                                 ["decode_main<bf16_t, 128, 4>", "decode_merge<bf16_t, 128, 4>"])
+                                 ["decode_main<bf16_t, 128, 4, true>", "decode_merge<bf16_t, 128, 4>"])
 
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seqs/s/layer, Llama-3.1-8B shape",
@@ -616,21 +642,28 @@ def main():
         "config": {"workload": wl.name, "num_seqs": S, "context_lens": "uniform 128..2048 (seed 2)",
                    "sum_context": sum_ctx, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "pool_blocks_per_layer": wl.num_blocks, "layers_rotated": L,
-                   "step": "kv_write + paged_attention_decode, one layer", "parallelism": "single GPU"},
+                   "step": "kv_write + paged_attention_decode, one layer, as one call "
+                           "(paged_attention_decode_append)", "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "useful_kv_ratio": round(sum_ctx / float(((st.context_lens.astype(np.int64) + B - 1) // B * B).sum()), 5),
         "seqs_per_s_per_layer": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_us_avg": round(dec_avg * 1e3, 2),
+        "two_call_step": {"calls": "kv_write, then paged_attention_decode", "ms_per_step": round(ms_two, 5),
+                          "value": round(kv_bytes / (ms_two * 1e-3) / 1e9, 2)},
+        "plain_decode": {"call": "paged_attention_decode (decode_main + decode_merge)",
+                         "us_avg": round(plain_avg * 1e3, 2), "achieved": round(plain_achieved, 2),
+                         "frac": round(plain_achieved / HBM_PEAK_GBPS, 4)},
         "decode_us_per_call_events": {"median": round(float(np.median(dec_ms)) * 1e3, 2),
                                       "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                                       "note": "an event pair around each call; each event adds its own gap"},
         "kv_write_us_avg": round(kvw_avg * 1e3, 2),
-        "kv_write_us_in_step": round((ms_per_step - dec_avg) * 1e3, 2),
+        "kv_write_us_in_two_call_step": round((ms_two - plain_avg) * 1e3, 2),
         "kv_write_note": "alone, back to back, the 64-token write is bound by the host's launch rate; "
-                         "kv_write_us_in_step = wall per step - decode average",
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode = decode_main + decode_merge",
+                         "kv_write_us_in_two_call_step = two-call wall per step - plain decode average",
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode_append = decode_main (append variant) + "
+                                               "decode_merge",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": int(round(tb)) if tb is not None else None, "traffic_unit": "bytes per launch"},

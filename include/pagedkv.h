@@ -156,6 +156,37 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                float scale, int dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Append and attend in one call: the kv_write of one new token per sequence
+ * ("08. PagedAttention", section "why the name": slot = block_table[logical
+ * block] * block_size + offset) followed by pkv_paged_attention_decode, for
+ * the usual decode step in which every sequence's new token is its last.
+ * For each sequence s with p = context_lens[s] - 1 >= 0:
+ *   - k_new[s], v_new[s] (device, [num_seqs][num_kv_heads][head_dim] of
+ *     dtype) are stored at slot block_tables[s][p / block_size] *
+ *     block_size + p % block_size of k_cache / v_cache;
+ *   - out[s] is the decode of q[s] over positions 0 .. p, position p taking
+ *     those K/V.
+ * The result, output and caches, is bit for bit that of pkv_kv_write of the
+ * same rows at those slots and then pkv_paged_attention_decode.  Other
+ * arguments, the workspace (sized by pkv_decode_workspace_size) and the
+ * errors are those of pkv_paged_attention_decode; k_new and v_new must be
+ * 16-byte aligned.
+ * The caller guarantees that
+ *   - context_lens[s] <= max_blocks_per_seq * block_size, and
+ *   - the slot belongs to sequence s alone in this call: a block shared by
+ *     several sequences is copied before a write (copy-on-write), as the
+ *     allocator arranges; another sequence reading the slot in the same call
+ *     could see either value.
+ * Sequences with context_lens[s] <= 0 write nothing and give zeros.  When
+ * the block id of position p lies outside [0, num_blocks) nothing is
+ * written and the sequence's rows come out NaN, as in the decode. */
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                                      int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* Sliding-window decode: as pkv_paged_attention_decode, but sequence s
  * attends only its last min(window, context_lens[s]) tokens (streaming with
  * a sliding window whose old blocks are reclaimed: intelliparadigm.com

@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     decode_workspace_size,
     kv_write,
     paged_attention_decode,
+    paged_attention_decode_append,
     paged_attention_prefill,
     swap_in,
     swap_out,

@@ -58,6 +58,8 @@ SIGNATURES = {
     "pkv_decode_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "pkv_paged_attention_decode": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_float, c_int, vp, c_size, vp]),
+    "pkv_paged_attention_decode_append": (c_int, [vp, vp, vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int,
+                                                  c_int, c_int, c_float, c_int, vp, c_size, vp]),
     "pkv_paged_attention_decode_window": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                                   c_int, c_int, c_float, c_int, vp, c_size, vp]),
     "pkv_paged_attention_decode_noalloc": (c_int, [vp, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int,

@@ -143,6 +143,35 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     return out
 
 
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, workspace: Optional[torch.Tensor] = None,
+                                  stream=None) -> torch.Tensor:
+    """kv_write of each sequence's new token (k_new/v_new[s], [num_seqs,
+    num_kv_heads, head_dim]) at position context_lens[s] - 1 through its
+    block table, then paged_attention_decode, in one call
+    (pkv_paged_attention_decode_append); bit for bit the two calls."""
+    N_, H, B, D = _cache_geometry(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q/out must be [num_seqs, num_heads, head_dim] of the cache dtype")
+    if k_new.shape != (S, H, D) or v_new.shape != (S, H, D) or k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim] of the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    mb = block_tables.shape[1]
+    if workspace is None:
+        workspace = torch.zeros(decode_workspace_size(S, Hq, H, D, B, mb, q.dtype), dtype=torch.uint8,
+                                device=q.device)
+    N.check(N.lib().pkv_paged_attention_decode_append(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32), mb,
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, H, D, B, N_, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+        "paged_attention_decode_append")
+    return out
+
+
 def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                                    v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                                    scale: float, stream=None) -> torch.Tensor:

@@ -162,7 +162,8 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
 static int decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
                        int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks, int window,
-                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                       const void* k_new = nullptr, const void* v_new = nullptr) {
   if (num_kv_heads <= 0) return PKV_ERR_INVALID;
   int st = check_attention(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                            dtype);
@@ -174,9 +175,11 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
       !aligned4(context_lens) || (workspace && !aligned16(workspace)))
     return PKV_ERR_ALIGN;
+  if ((k_new != nullptr) != (v_new != nullptr)) return PKV_ERR_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
   return pkv::launch_decode(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                             num_heads, num_kv_heads, head_dim, block_size, num_blocks, window, scale, dtype,
-                            workspace, workspace_bytes, (hipStream_t)stream);
+                            workspace, workspace_bytes, (hipStream_t)stream, k_new, v_new);
 }
 
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -187,6 +190,18 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, 0, scale, dtype, workspace, workspace_bytes,
                      stream);
+}
+
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                                      int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID;
+  return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, 0, scale, dtype, workspace, workspace_bytes,
+                     stream, k_new, v_new);
 }
 
 int pkv_paged_attention_decode_window(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -59,6 +59,10 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   float* part;  // two partial slots of PSZ floats per wavefront
   int2* jobs;   // per wavefront: (unit, last wavefront) of the unit it starts, or (-1, 0)
+  // Append variant: K/V rows [S][Hkv][D] of the token at position ctx - 1 of
+  // each sequence, attended from here and stored into the cache.
+  const void* k_new;
+  const void* v_new;
   int S, Hq, Hkv, max_blocks, num_blocks, log2B, nW;
   int window;   // > 0: attend only the last `window` tokens of each context
   float scale_log2;
@@ -173,6 +177,7 @@ struct Chunk {
   uint4 v[DShape<T, D, G>::J];
   int ok;   // bit j: row j holds a valid token with a valid block
   int bad;  // bit j: row j is a valid token whose block id is out of range
+  long long app;  // append variant: byte offset of the new row in the kv head's cache, or -1
 };
 
 // One (kv head, sequence) unit as a wavefront sees it.  Lane i of win0 /
@@ -186,6 +191,8 @@ struct Unit {
   int lo, cf;            // first attended token (sliding window) and its chunk
   int nblk, wbase;
   int win0, win1;
+  const char* kn;  // append variant: this unit's new K and V rows
+  const char* vn;
   uint4 qv[G];
 };
 
@@ -197,7 +204,7 @@ __device__ __forceinline__ int load_window(const Unit<T, D, G>& u, int base, int
 
 // Set up unit (h, s) starting at global chunk g0: issue the loads of its
 // table window and query rows (nothing waits for them here).
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool APP>
 __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a, int h, int s, int ctx, int g0,
                                           int c0, int lane) {
   using SH = DShape<T, D, G>;
@@ -216,6 +223,11 @@ __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a,
   u.wbase = ((c0 + u.cf) * SH::NT) >> a.log2B;
   u.win0 = load_window(u, u.wbase, lane);
   u.win1 = load_window(u, u.wbase + 64, lane);
+  if constexpr (APP) {
+    const size_t no = ((size_t)s * a.Hkv + h) * rowb;
+    u.kn = (const char*)a.k_new + no;
+    u.vn = (const char*)a.v_new + no;
+  }
   const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + (lane % SH::LR) * 16;
 #pragma unroll
   for (int g = 0; g < G; ++g) u.qv[g] = *(const uint4*)(qp + g * rowb);
@@ -225,8 +237,11 @@ __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a,
 // of unit u.  Rows outside [lo, ctx), or whose block id is out of range, are
 // zero; the latter are flagged so that the output turns into NaN instead of
 // reading outside the pool.  Table entries of blocks wholly before lo are
-// never read (a sliding window may have released them).
-template <typename T, int D, int G>
+// never read (a sliding window may have released them).  In the append
+// variant the row of position ctx - 1 comes from the unit's new K/V row
+// instead of the cache, and the chunk notes where that row goes in the
+// cache (stored once the chunk has been computed).
+template <typename T, int D, int G, bool APP>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u, const DecodeArgs& a, int c,
                                            int lane) {
   using SH = DShape<T, D, G>;
@@ -251,6 +266,9 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
   const size_t blkb = (size_t)a.Hkv << a.log2B;  // rows per physical block (all heads)
   ch.ok = 0;
   ch.bad = 0;
+  // row of the new token, in this chunk if below NT (the same for every lane)
+  const int rnew = u.ctx - 1 - t0;
+  if constexpr (APP) ch.app = -1;
   if (SH::NT <= B) {
     // the whole chunk lies in one block: one uniform table entry, one
     // uniform base address, a 32-bit offset per lane
@@ -261,6 +279,9 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
     const char* kp = u.kb + ub;
     const char* vp = u.vb + ub;
     const int full = t0 >= u.lo && t0 + SH::NT <= u.ctx;
+    if constexpr (APP) {
+      if (bok && rnew < SH::NT) ch.app = (long long)(ub + (size_t)rnew * rowb);
+    }
     const unsigned loff = (unsigned)(rg * D * SH::ES + cl * 16);
 #pragma unroll
     for (int j = 0; j < SH::J; ++j) {
@@ -268,8 +289,16 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       const unsigned off = loff + (unsigned)(j * SH::RW * D * SH::ES);
       const bool in = t0 + r >= u.lo && t0 + r < u.ctx;
       if (bok && (full || in)) {
-        ch.k[j] = load_stream(kp + off);
-        ch.v[j] = load_stream(vp + off);
+        const char* ks = kp + off;
+        const char* vs = vp + off;
+        if constexpr (APP) {
+          if (r == rnew) {
+            ks = u.kn + cl * 16;
+            vs = u.vn + cl * 16;
+          }
+        }
+        ch.k[j] = load_stream(ks);
+        ch.v[j] = load_stream(vs);
         ch.ok |= 1 << j;
       } else {
         ch.k[j] = make_uint4(0, 0, 0, 0);
@@ -278,6 +307,14 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       }
     }
   } else {
+    if constexpr (APP) {
+      if (rnew < SH::NT) {
+        const int wn = ((u.ctx - 1) >> a.log2B) - u.wbase;  // the chunk holds it, so it is in the window
+        const int bn = wn < 64 ? __builtin_amdgcn_readlane(u.win0, wn) : __builtin_amdgcn_readlane(u.win1, wn - 64);
+        if ((unsigned)bn < (unsigned)a.num_blocks)
+          ch.app = (long long)(((size_t)bn * blkb + ((u.ctx - 1) & (B - 1))) * rowb);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < SH::J; ++j) {
       const int t = t0 + rg + j * SH::RW;
@@ -290,8 +327,16 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
       if (t >= u.lo && t < u.ctx) {
         if ((unsigned)blk < (unsigned)a.num_blocks) {
           const size_t off = ((size_t)blk * blkb + (t & (B - 1))) * rowb + cl * 16;
-          ch.k[j] = load_stream(u.kb + off);
-          ch.v[j] = load_stream(u.vb + off);
+          const char* ks = u.kb + off;
+          const char* vs = u.vb + off;
+          if constexpr (APP) {
+            if (t - t0 == rnew) {
+              ks = u.kn + cl * 16;
+              vs = u.vn + cl * 16;
+            }
+          }
+          ch.k[j] = load_stream(ks);
+          ch.v[j] = load_stream(vs);
           ch.ok |= 1 << j;
         } else {
           ch.bad |= 1 << j;
@@ -474,7 +519,27 @@ __device__ __forceinline__ bool next_unit(const DecodeArgs& a, const int* lc, in
   }
 }
 
+// Store the new row of the unit's last chunk into the cache (append
+// variant): the lanes that loaded it from the new K/V hold it in the chunk's
+// registers, which the computation has already waited for.
 template <typename T, int D, int G>
+__device__ __forceinline__ void store_new_row(const Chunk<T, D, G>& ch, const Unit<T, D, G>& u, int c, int lane) {
+  using SH = DShape<T, D, G>;
+  if (ch.app < 0) return;
+  const int rnew = u.ctx - 1 - (c + u.cf) * SH::NT;
+  const int rg = lane / SH::LR;
+  const size_t o = (size_t)ch.app + (lane % SH::LR) * 16;
+  // a test per lane and load (not an index computed once), so that the
+  // registers are never indexed at run time
+#pragma unroll
+  for (int j = 0; j < SH::J; ++j)
+    if (rg + j * SH::RW == rnew) {
+      *(uint4*)(const_cast<char*>(u.kb) + o) = ch.k[j];
+      *(uint4*)(const_cast<char*>(u.vb) + o) = ch.v[j];
+    }
+}
+
+template <typename T, int D, int G, bool APP>
 __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   using SH = DShape<T, D, G>;
   constexpr int E = SH::E;
@@ -581,13 +646,13 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
 
   Unit<T, D, G> cur, nxt;
   int c = rem - P;  // chunk of `cur` being computed
-  open_unit(cur, a, h, s, ctx_of(a, lc, maxctx, s), gstart - c, c, lane);
+  open_unit<T, D, G, APP>(cur, a, h, s, ctx_of(a, lc, maxctx, s), gstart - c, c, lane);
   int seg_c0 = c;  // first chunk of cur in this wavefront's share
   bool have_next = false;
   {
     int h2 = h, s2 = s, ctx2 = 0;
     if (cur.g0 + cur.n < gend && next_unit(a, lc, maxctx, h2, s2, ctx2)) {
-      open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
+      open_unit<T, D, G, APP>(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
       have_next = true;
     }
   }
@@ -604,10 +669,13 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   // Returns false when the share is done.
   auto step = [&](Chunk<T, D, G>& cb, Chunk<T, D, G>& nb, int i) -> bool {
     if (i + 1 < gend) {
-      if (c + 1 < cur.n) load_chunk(nb, cur, a, c + 1, lane);
-      else load_chunk(nb, nxt, a, 0, lane);
+      if (c + 1 < cur.n) load_chunk<T, D, G, APP>(nb, cur, a, c + 1, lane);
+      else load_chunk<T, D, G, APP>(nb, nxt, a, 0, lane);
     }
     compute_chunk<T, D, G>(cb, cur.qv, lane, a.scale_log2, m, lsum, acc, L);
+    if constexpr (APP) {
+      if (c == cur.n - 1) store_new_row<T, D, G>(cb, cur, c, lane);
+    }
     ++c;
     if (c < cur.n && i + 1 < gend) return true;
     const int mode = seg_c0 > 0 ? 1 : (c < cur.n ? 2 : 0);
@@ -620,7 +688,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
     have_next = false;
     int h2 = cur.h, s2 = cur.s, ctx2 = 0;
     if (cur.g0 + cur.n < gend && next_unit(a, lc, maxctx, h2, s2, ctx2)) {
-      open_unit(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
+      open_unit<T, D, G, APP>(nxt, a, h2, s2, ctx2, cur.g0 + cur.n, 0, lane);
       have_next = true;
     }
     m = -INFINITY;
@@ -633,7 +701,7 @@ __global__ __launch_bounds__(256) void decode_main(DecodeArgs a) {
   };
 
   Chunk<T, D, G> ca, cb;
-  load_chunk(ca, cur, a, c, lane);
+  load_chunk<T, D, G, APP>(ca, cur, a, c, lane);
   for (int i = gstart; i < gend; i += 2) {
     if (!step(ca, cb, i)) break;
     if (i + 1 >= gend || !step(cb, ca, i + 1)) break;
@@ -720,6 +788,7 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 struct DecodeKernels {
   const void* main;
+  const void* main_app;  // the append variant
   const void* merge;
   int nt;
   int psz;
@@ -728,7 +797,8 @@ struct DecodeKernels {
 template <typename T, int D, int G>
 static DecodeKernels kernels_for() {
   using SH = DShape<T, D, G>;
-  return {(const void*)decode_main<T, D, G>, (const void*)decode_merge<T, D, G>, SH::NT, SH::PSZ};
+  return {(const void*)decode_main<T, D, G, false>, (const void*)decode_main<T, D, G, true>,
+          (const void*)decode_merge<T, D, G>, SH::NT, SH::PSZ};
 }
 static bool pick(int dtype, int D, int G, DecodeKernels* k) {
 #define PKV_CASE(TT, DD, GG)                      \
@@ -758,13 +828,21 @@ bool decode_supported(int dtype, int head_dim, int group) {
 
 // Number of wavefronts of the persistent grid: a fixed number of
 // workgroups per compute unit (PKV_DECODE_WG_PER_CU overrides the device's
-// occupancy limit), never more than the chunks there can be.
-static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B) {
+// occupancy limit), never more than the chunks there can be.  The append
+// variant takes the lower occupancy of its kernel and the plain one, so its
+// grid never needs more workspace than the plain decode's.
+static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B, bool app = false) {
   const DeviceInfo& dev = device_info();
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 64 * kWavesPerWG, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
+  if (app) {
+    int pa = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pa, k.main_app, 64 * kWavesPerWG, 0) != hipSuccess || pa < 1)
+      pa = 1;
+    per_cu = std::min(per_cu, pa);
+  }
   const int force = tuning_int("PKV_DECODE_WG_PER_CU", 0);
   if (force > 0) per_cu = std::min(force, 8);
   long long wgs = (long long)per_cu * std::max(dev.num_cus, 1);
@@ -794,10 +872,12 @@ size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_b
 
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                   int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
-                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream,
+                  const void* k_new, const void* v_new) {
   DecodeKernels k;
   if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
-  const int nW = decode_waves(k, S, Hkv, max_blocks, B);
+  if (k_new != nullptr && window > 0) return -2;
+  const int nW = decode_waves(k, S, Hkv, max_blocks, B, k_new != nullptr);
   size_t jobs_off;
   const size_t need = workspace_layout(k, nW, &jobs_off);
   if (ws == nullptr || ws_bytes < need) return -7;
@@ -810,6 +890,8 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.ctx_lens = ctx;
   a.part = (float*)ws;
   a.jobs = (int2*)((char*)ws + jobs_off);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.S = S;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -821,7 +903,8 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int grid = nW / kWavesPerWG;
-  hipLaunchKernelGGL((void (*)(DecodeArgs))k.main, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
+  const void* main = k_new != nullptr ? k.main_app : k.main;
+  hipLaunchKernelGGL((void (*)(DecodeArgs))main, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -6;
   hipLaunchKernelGGL((void (*)(DecodeArgs))k.merge, dim3(grid), dim3(64 * kWavesPerWG), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -6;

@@ -37,9 +37,11 @@ int launch_gather_units(const void* pool_a, const void* pool_b, const int32_t* i
 
 bool decode_supported(int dtype, int head_dim, int group);
 size_t decode_workspace_bytes(int dtype, int D, int G, int S, int Hkv, int max_blocks, int B);
+// k_new / v_new non-null: the append variant (window must be 0).
 int launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                   int max_blocks, const int32_t* ctx, int S, int Hq, int Hkv, int D, int B, int num_blocks,
-                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+                  int window, float scale, int dtype, void* ws, size_t ws_bytes, hipStream_t stream,
+                  const void* k_new = nullptr, const void* v_new = nullptr);
 
 // Size of the library's own decode scratch array (per GPU).
 constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
