@@ -485,6 +485,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="run the step untimed this long before the warmup steps")
     ap.add_argument("--prefill-steps", type=int, default=40)
     ap.add_argument("--prefill-layers", type=int, default=40)
     ap.add_argument("--no-prefill", action="store_true")
@@ -585,6 +587,17 @@ def main():
     # kv_write then paged_attention_decode)
     step = append_decode
 
+    # Settle: the step runs back to back, untimed, for --settle-ms before
+    # the warmup steps.  The first milliseconds of back-to-back work after the
+    # setup run 1.5-3 us per step slower than the rest, which a short timed
+    # region would otherwise measure.
+    n_settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        for _ in range(50):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -634,6 +647,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "settle": {"ms": args.settle_ms, "steps": n_settle,
+                   "note": "untimed steps before the warmup, so that the timed region starts at steady state"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/pagedkv.h"
 #include "kernels.h"
@@ -32,6 +33,26 @@ const DeviceInfo& device_info() {
     }
   }
   return d;
+}
+
+int occupancy(const void* kernel, int threads) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int threads;
+    int blocks;
+  };
+  static std::vector<Entry> known;
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : known)
+    if (e.dev == dev && e.kernel == kernel && e.threads == threads) return e.blocks;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) return 1;
+  known.push_back({dev, kernel, threads, n});
+  return n;
 }
 
 int tuning_int(const char* name, int dflt) {

@@ -833,16 +833,8 @@ bool decode_supported(int dtype, int head_dim, int group) {
 // grid never needs more workspace than the plain decode's.
 static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B, bool app = false) {
   const DeviceInfo& dev = device_info();
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 64 * kWavesPerWG, 0) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  if (app) {
-    int pa = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pa, k.main_app, 64 * kWavesPerWG, 0) != hipSuccess || pa < 1)
-      pa = 1;
-    per_cu = std::min(per_cu, pa);
-  }
+  int per_cu = occupancy(k.main, 64 * kWavesPerWG);
+  if (app) per_cu = std::min(per_cu, occupancy(k.main_app, 64 * kWavesPerWG));
   const int force = tuning_int("PKV_DECODE_WG_PER_CU", 0);
   if (force > 0) per_cu = std::min(force, 8);
   long long wgs = (long long)per_cu * std::max(dev.num_cus, 1);

@@ -20,8 +20,12 @@ struct DeviceInfo {
 // Properties of the current device (queried once per device).
 const DeviceInfo& device_info();
 
-// Integer tuning knob from the environment (read once), or dflt.
+// Integer tuning knob from the environment (read at each call), or dflt.
 int tuning_int(const char* name, int dflt);
+
+// Workgroups of `threads` threads of `kernel` that fit on one compute unit of
+// the current device (at least 1), queried once per device and kernel.
+int occupancy(const void* kernel, int threads);
 
 int launch_kv_write(const void* k_new, const void* v_new, const int32_t* slots, int num_tokens, void* k_cache,
                     void* v_cache, int num_blocks, int Hkv, int B, int D, int elem_bytes, hipStream_t stream);

@@ -767,8 +767,7 @@ int launch_prefill(void* out, const void* q, const int32_t* cu_q_lens, int total
   if (items <= 0) return 0;
   if (items > 0x7fffffffLL) return -2;
   const void* kfn = D == 128 ? (const void*)prefill_kernel<128> : (const void*)prefill_kernel<64>;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kPThreads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int per_cu = occupancy(kfn, kPThreads);
   const long long grid = std::min(items, (long long)per_cu * std::max(device_info().num_cus, 1));
   const dim3 g((unsigned)grid), b(kPThreads);
   if (D == 128)
