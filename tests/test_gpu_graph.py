@@ -1,4 +1,5 @@
-"""The decode step (kv_write, then paged_attention_decode) captured in a HIP
+"""The decode step (kv_write, then paged_attention_decode; or the two as one
+paged_attention_decode_append call) captured in a HIP
 graph: the library's calls only enqueue kernels on the caller's stream (no
 allocation, no memset, no synchronisation), so they can be captured.  Every
 replay, with eager work and synchronisations between replays, must equal the
@@ -64,5 +65,73 @@ def test_decode_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for li in range(layers):
             assert torch.equal(outs[li].view(torch.int16), ref[li].view(torch.int16)), (rep, li)
+        steps()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_append_step_graph_replays_match_eager():
+    """The same step as one paged_attention_decode_append call per layer,
+    captured: before every replay the new tokens' slots are poisoned again,
+    so each replay must write them back as well as reproduce the outputs."""
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    print("[gpu] graph capture of paged_attention_decode_append", flush=True)
+    sys.stdout.flush()
+    wl = W.llama_decode(42, 24, 1, 1500, 2048, "llama-graph-append")
+    st = driver.run_script(wl)
+    S, Hq, Hkv, D, B = len(wl.batch), wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    layers = 3
+    kps, vps = [st.k_pool], [st.v_pool]
+    for _ in range(1, layers):
+        kps.append(st.k_pool.clone())
+        vps.append(st.v_pool.clone())
+    q = driver.to_device(wl.q, wl.dtype, "cuda")
+    outs = [torch.empty_like(q) for _ in range(layers)]
+    dec = wl.steps[-1]
+    kn = driver.to_device(np.concatenate([op.k for op in dec.ops]), wl.dtype, "cuda")
+    vn = driver.to_device(np.concatenate([op.v for op in dec.ops]), wl.dtype, "cuda")
+    ws = torch.zeros(api.decode_workspace_size(S, Hq, Hkv, D, B, wl.max_blocks_per_seq, q.dtype),
+                     dtype=torch.uint8, device="cuda")
+    new = [(int(st.tables[i][(int(n) - 1) // B]), (int(n) - 1) % B) for i, n in enumerate(st.context_lens)]
+
+    def poison():
+        for li in range(layers):
+            for blk, off in new:
+                kps[li][blk, :, off, :] = float("nan")
+                vps[li][blk, :, off, :] = float("nan")
+
+    def steps():
+        for li in range(layers):
+            api.paged_attention_decode_append(outs[li], q, kn, vn, kps[li], vps[li], st.tables_dev, st.lens_dev,
+                                              float(wl.scale), workspace=ws)
+
+    poison()
+    steps()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    ref_k = [driver.pool_bits(p) for p in kps]
+    ref_v = [driver.pool_bits(p) for p in vps]
+    assert np.array_equal(ref_k[0], driver.pool_bits(st.k_pool))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        poison()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li in range(layers):
+            assert torch.equal(outs[li].view(torch.int16), ref[li].view(torch.int16)), (rep, li)
+            assert np.array_equal(driver.pool_bits(kps[li]), ref_k[li]), (rep, li)
+            assert np.array_equal(driver.pool_bits(vps[li]), ref_v[li]), (rep, li)
         steps()  # eager work between replays
         torch.cuda.synchronize()
