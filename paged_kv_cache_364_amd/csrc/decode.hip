@@ -829,12 +829,13 @@ bool decode_supported(int dtype, int head_dim, int group) {
 // Number of wavefronts of the persistent grid: a fixed number of
 // workgroups per compute unit (PKV_DECODE_WG_PER_CU overrides the device's
 // occupancy limit), never more than the chunks there can be.  The append
-// variant takes the lower occupancy of its kernel and the plain one, so its
-// grid never needs more workspace than the plain decode's.
-static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B, bool app = false) {
+// variant runs on the plain decode's grid, so that both split the chunks at
+// the same points and round alike; where it fits fewer workgroups per
+// compute unit (some small head dims), the rest wait for a slot, which is
+// safe because no workgroup of the pass waits for another.
+static int decode_waves(const DecodeKernels& k, int S, int Hkv, int max_blocks, int B) {
   const DeviceInfo& dev = device_info();
   int per_cu = occupancy(k.main, 64 * kWavesPerWG);
-  if (app) per_cu = std::min(per_cu, occupancy(k.main_app, 64 * kWavesPerWG));
   const int force = tuning_int("PKV_DECODE_WG_PER_CU", 0);
   if (force > 0) per_cu = std::min(force, 8);
   long long wgs = (long long)per_cu * std::max(dev.num_cus, 1);
@@ -869,7 +870,7 @@ int launch_decode(void* out, const void* q, const void* k_cache, const void* v_c
   DecodeKernels k;
   if (!pick(dtype, D, Hq / Hkv, &k)) return -2;
   if (k_new != nullptr && window > 0) return -2;
-  const int nW = decode_waves(k, S, Hkv, max_blocks, B, k_new != nullptr);
+  const int nW = decode_waves(k, S, Hkv, max_blocks, B);
   size_t jobs_off;
   const size_t need = workspace_layout(k, nW, &jobs_off);
   if (ws == nullptr || ws_bytes < need) return -7;

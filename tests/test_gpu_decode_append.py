@@ -132,6 +132,9 @@ def test_shared_prefix_full():
     ("bf16", 128, 32, 8, 256), ("bf16", 64, 16, 2, 16), ("bf16", 128, 8, 8, 16), ("bf16", 128, 16, 8, 16),
     ("bf16", 64, 8, 1, 16), ("f32", 128, 8, 2, 16), ("f32", 64, 8, 8, 4), ("f32", 32, 16, 2, 2),
     ("f32", 128, 16, 2, 64),
+    # shapes whose append instantiation fits fewer workgroups per compute
+    # unit than the plain one: the call must still split like the decode
+    ("bf16", 16, 16, 8, 32), ("bf16", 32, 8, 4, 16), ("bf16", 16, 4, 4, 4), ("f32", 16, 8, 2, 8),
 ])
 def test_shapes(dtype, d, hq, hkv, b):
     # contexts end at every offset of a block, including the first slot of a
