@@ -171,14 +171,15 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
  * arguments, the workspace (sized by pkv_decode_workspace_size) and the
  * errors are those of pkv_paged_attention_decode; k_new and v_new must be
  * 16-byte aligned.
- * The caller guarantees that
- *   - context_lens[s] <= max_blocks_per_seq * block_size, and
- *   - the slot belongs to sequence s alone in this call: a block shared by
- *     several sequences is copied before a write (copy-on-write), as the
- *     allocator arranges; another sequence reading the slot in the same call
- *     could see either value.
- * Sequences with context_lens[s] <= 0 write nothing and give zeros.  When
- * the block id of position p lies outside [0, num_blocks) nothing is
+ * The caller guarantees that the slot belongs to sequence s alone in this
+ * call: a block shared by several sequences is copied before a write
+ * (copy-on-write), as the allocator arranges; another sequence reading the
+ * slot in the same call could see either value.
+ * Sequences with context_lens[s] <= 0 write nothing and give zeros.  Those
+ * with context_lens[s] > max_blocks_per_seq * block_size have no slot for
+ * the new token: they write nothing and attend their first
+ * max_blocks_per_seq * block_size tokens from the cache, as the decode does.
+ * When the block id of position p lies outside [0, num_blocks), nothing is
  * written and the sequence's rows come out NaN, as in the decode. */
 int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
                                       void* k_cache, void* v_cache, const int32_t* block_tables,

@@ -191,7 +191,7 @@ struct Unit {
   int lo, cf;            // first attended token (sliding window) and its chunk
   int nblk, wbase;
   int win0, win1;
-  const char* kn;  // append variant: this unit's new K and V rows
+  const char* kn;  // append variant: this unit's new K and V rows (null: none)
   const char* vn;
   uint4 qv[G];
 };
@@ -227,6 +227,9 @@ __device__ __forceinline__ void open_unit(Unit<T, D, G>& u, const DecodeArgs& a,
     const size_t no = ((size_t)s * a.Hkv + h) * rowb;
     u.kn = (const char*)a.k_new + no;
     u.vn = (const char*)a.v_new + no;
+    // a context longer than the table (clamped to it for the attention) has
+    // no slot for its new token: nothing is taken from the new rows or stored
+    if (a.ctx_lens[s] > (a.max_blocks << a.log2B)) u.kn = u.vn = nullptr;
   }
   const char* qp = (const char*)a.q + ((size_t)s * a.Hq + (size_t)h * G) * rowb + (lane % SH::LR) * 16;
 #pragma unroll
@@ -267,7 +270,7 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G>& ch, Unit<T, D, G>& u,
   ch.ok = 0;
   ch.bad = 0;
   // row of the new token, in this chunk if below NT (the same for every lane)
-  const int rnew = u.ctx - 1 - t0;
+  const int rnew = APP && u.kn != nullptr ? u.ctx - 1 - t0 : SH::NT;
   if constexpr (APP) ch.app = -1;
   if (SH::NT <= B) {
     // the whole chunk lies in one block: one uniform table entry, one

@@ -222,3 +222,27 @@ def test_argument_errors():
         ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
         api.paged_attention_decode_append(out, q, kn, vn, st.k_pool, st.v_pool, st.tables_dev, st.lens_dev,
                                           float(wl.scale), workspace=ws)
+
+
+def test_context_past_the_table_writes_nothing():
+    # sequence 1 fills its table exactly; a context longer than that has no
+    # slot for a new token, so the call attends the clamped context (as the
+    # decode does) and neither reads nor stores the new row
+    lens = [40, 64, 33]
+    wl = W.decode_workload("append-past", 75, lens, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                           num_blocks=64, dtype="bf16", max_blocks_per_seq=4)
+    st = driver.run_script(wl)
+    over = torch.from_numpy(np.asarray([40, 64 + 7, 33], dtype=np.int32)).cuda()
+    q = driver.to_device(wl.q, wl.dtype, "cuda")
+    kn, vn = new_tokens(wl)
+    kn[1] = float("nan")
+    vn[1] = float("nan")
+    ref = torch.empty_like(q)
+    api.paged_attention_decode(ref, q, st.k_pool, st.v_pool, st.tables_dev, over, float(wl.scale))
+    kp, vp = st.k_pool.clone(), st.v_pool.clone()
+    out = torch.empty_like(q)
+    api.paged_attention_decode_append(out, q, kn, vn, kp, vp, st.tables_dev, over, float(wl.scale))
+    torch.cuda.synchronize()
+    assert np.isfinite(driver.out_to_f64(out)).all()
+    assert np.array_equal(bits(out), bits(ref))
+    assert np.array_equal(bits(kp), bits(st.k_pool)) and np.array_equal(bits(vp), bits(st.v_pool))
