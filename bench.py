@@ -67,6 +67,20 @@ def host_description(np):
             "numpy": np.__version__, "blas": blas}
 
 
+def settle(torch, fn, ms, batch):
+    """Run fn(i) back to back, untimed, for at least `ms` milliseconds, so
+    that what is timed next runs at the clocks a busy GPU holds; returns
+    the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < ms * 1e-3:
+        for _ in range(batch):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def timed_calls(torch, fn, n, warmup, stream, per_call=True):
     """Average time per call (ms) of ``fn(i)``: one pair of events, recorded
     on the stream the kernels run on, around n calls back to back (an event
@@ -155,8 +169,13 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         li = i % L
         api.kv_write(kn, vn, slots, kps[li], vps[li])
 
-    # the matrix cores' clocks take a few tens of calls to settle
-    pf_ms, pf_all = timed_calls(torch, prefill, args.prefill_steps, max(args.warmup, 40), stream)
+    # The clocks climb while the GPU is busy: 40 calls timed right after the
+    # setup (and 40 warmup calls) run several percent slower than the same
+    # calls after ~100 ms of back-to-back work.  Both are reported; the
+    # roofline takes the settled figure.
+    cold_ms, _ = timed_calls(torch, prefill, args.prefill_steps, max(args.warmup, 40), stream, per_call=False)
+    n_settle = settle(torch, prefill, args.settle_ms, 8)
+    pf_ms, pf_all = timed_calls(torch, prefill, args.prefill_steps, args.warmup, stream)
     kw_ms, _ = timed_calls(torch, write, args.prefill_steps, args.warmup, stream)
     tflops = flops / (pf_ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {pf_ms * 1e3:.1f} us avg, {tflops:.1f} TFLOP/s; kv_write of the chunk "
@@ -179,6 +198,9 @@ def prefill_leg(args, torch, np, api, driver, workloads, dev):
         "workload": wl.name, "num_seqs": S, "chunk": int(C[0]), "prefix_lens": "uniform 0..1536 (seed 5)",
         "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": B, "layers_rotated": L,
         "prefill_us_avg": round(pf_ms * 1e3, 2),
+        "prefill_us_avg_unsettled": round(cold_ms * 1e3, 2),
+        "settle": {"ms": args.settle_ms, "calls": n_settle,
+                   "note": "untimed calls between the unsettled and the settled measurement"},
         "prefill_us_per_call_events": {"median": round(float(np.median(pf_all)) * 1e3, 2),
                                        "p10": round(float(np.percentile(pf_all, 10)) * 1e3, 2),
                                        "p90": round(float(np.percentile(pf_all, 90)) * 1e3, 2)},
@@ -485,8 +507,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--settle-ms", type=float, default=50.0,
-                    help="run the step untimed this long before the warmup steps")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="run the step (and the prefill) untimed this long before their warmup")
     ap.add_argument("--prefill-steps", type=int, default=40)
     ap.add_argument("--prefill-layers", type=int, default=40)
     ap.add_argument("--no-prefill", action="store_true")
@@ -589,15 +611,9 @@ def main():
 
     # Settle: the step runs back to back, untimed, for --settle-ms before
     # the warmup steps.  The first milliseconds of back-to-back work after the
-    # setup run 1.5-3 us per step slower than the rest, which a short timed
-    # region would otherwise measure.
-    n_settle = 0
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
-        for _ in range(50):
-            step(n_settle)
-            n_settle += 1
-        torch.cuda.synchronize()
+    # setup run 1.5-3 us per step slower than the rest (the clocks climb while
+    # the GPU is busy), which a short timed region would otherwise measure.
+    n_settle = settle(torch, step, args.settle_ms, 50)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
