@@ -151,6 +151,28 @@ def test_decode_rejects_bad_arguments():
     assert L.pkv_decode_workspace_size(4, 8, 2, 16, 16, 4, 1) == 0
 
 
+def test_decode_append_rejects_bad_arguments():
+    L = N.lib()
+    p = fake()
+    args = dict(out=p, q=p, kn=p, vn=p, k=p, v=p, t=p, mb=4, ctx=p, S=2, Hq=8, Hkv=2, D=128, B=16, N=64, scale=0.1,
+                dt=1, ws=p, wsb=1 << 20, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.pkv_paged_attention_decode_append(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["t"],
+                                                   a["mb"], a["ctx"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                                                   a["N"], a["scale"], a["dt"], a["ws"], a["wsb"], a["st"])
+    assert call(kn=None) == N.PKV_ERR_INVALID       # the new rows are required
+    assert call(vn=None) == N.PKV_ERR_INVALID
+    assert call(kn=fake(0x100008)) == N.PKV_ERR_ALIGN
+    assert call(vn=fake(0x100004)) == N.PKV_ERR_ALIGN
+    assert call(Hq=7) == N.PKV_ERR_INVALID
+    assert call(Hq=6) == N.PKV_ERR_UNSUPPORTED
+    assert call(q=None) == N.PKV_ERR_INVALID
+    assert call(k=fake(0x100004)) == N.PKV_ERR_ALIGN
+    assert call(S=0, kn=None, vn=None) == N.PKV_OK  # nothing to do
+
+
 def test_prefill_rejects_bad_arguments():
     L = N.lib()
     p = fake()
