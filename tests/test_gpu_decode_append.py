@@ -246,3 +246,14 @@ def test_context_past_the_table_writes_nothing():
     assert np.isfinite(driver.out_to_f64(out)).all()
     assert np.array_equal(bits(out), bits(ref))
     assert np.array_equal(bits(kp), bits(st.k_pool)) and np.array_equal(bits(vp), bits(st.v_pool))
+
+
+@pytest.mark.parametrize("n,hi", [(2048, 64), (4100, 24)])
+def test_many_short_sequences(n, hi):
+    # batches past the 512 sequences whose lengths the decode keeps in LDS:
+    # the lengths are read from memory instead
+    rng = np.random.default_rng(1900 + n)
+    lens = [int(x) for x in rng.integers(1, hi + 1, size=n)]
+    wl = W.decode_workload(f"append-short-{n}", 1901 + n, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, num_blocks=8192, dtype="bf16")
+    check_append(wl)
