@@ -720,7 +720,12 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   using SH = DShape<T, D, G>;
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+  // the main pass's mapping of workgroups to XCDs, so that a job's merge
+  // runs on the XCD whose L2 holds most of its partials
+  int wg = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int w = wg * kWavesPerWG + (threadIdx.x >> 6);
   if (w >= a.nW) return;
   const int2 job = a.jobs[w];
   if (job.x < 0 || lane >= SH::OUT_LANES) return;
