@@ -204,3 +204,18 @@ def test_gather_units_rejects_bad_arguments():
     assert L.pkv_gather_units(None, p, p, 4, 4, 64, p, 16, None) == N.PKV_ERR_INVALID
     assert L.pkv_gather_units(fake(0x100004), None, p, 4, 4, 64, p, 16, None) == N.PKV_ERR_ALIGN
     assert L.pkv_gather_units(p, None, p, 0, 4, 64, p, 16, None) == N.PKV_OK
+
+
+def test_header_compiles_as_c(tmp_path):
+    """The boundary is a C ABI: the header compiles as C99, warning-free."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "pagedkv.h"\nint main(void) { return pkv_abi_version() == PKV_ABI_VERSION ? 0 : 1; }\n')
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-c", str(src), "-o", str(tmp_path / "use_header.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
