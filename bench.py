@@ -92,9 +92,12 @@ def timed_calls(torch, fn, n, warmup, stream, per_call=True):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one untimed call first: the GPU is busy when it reaches e0, so the host's
+    # launch latency of the first timed call does not land between the events
+    fn(warmup)
     e0.record(stream)
     for i in range(n):
-        fn(warmup + i)
+        fn(warmup + 1 + i)
     e1.record(stream)
     torch.cuda.synchronize()
     avg = e0.elapsed_time(e1) / n
@@ -103,7 +106,7 @@ def timed_calls(torch, fn, n, warmup, stream, per_call=True):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for i in range(n):
             evs[i][0].record(stream)
-            fn(warmup + n + i)
+            fn(warmup + 1 + n + i)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
         ts = [a.elapsed_time(b) for a, b in evs]
